@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Fixed-budget ragged pass on one MI355X: tokens/s of the whole hot path.
+
+One step = one pass of the method over one synthetic batch: Dynamic SplitFuse composition
+and block allocation (host, C++), upload of the ragged descriptors and work list, kv_append
+(HIP) and ragged blocked attention (HIP), all through the C ABI.  Inputs are resident in
+HBM before timing starts; every step recomposes the same pass from the same starting state,
+so the K timed steps repeat identical work.
+
+Default workload: LLaMA-2-7B attention shape (32 heads of 128, blocks of 64), a 2048-token
+budget filled by 24 decode tokens plus prompt chunks.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2|decode|chunked|mistral]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ragged-pass tokens/s at fixed budget; KV HBM GB/s & MFMA % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+F32_VALU_PEAK_TFLOPS = 157.3
+WORKLOADS = {"llama2": 2, "decode": 3, "chunked": 4, "mistral": 5}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("fg_kernels.hip", "fg_internal.h"):
+        with open(os.path.join(ROOT, "ragged_blocked_kv_splitfuse_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama2", choices=sorted(WORKLOADS))
+    ap.add_argument("--chunk-pass", type=int, default=31,
+                    help="chunked workload: which 512-token pass (0..31) a step runs")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--seed", type=int, default=None)
+    return ap.parse_args()
+
+
+def setup(args):
+    import numpy as np
+    import torch
+    from ragged_blocked_kv_splitfuse_amd import fg, workloads as wl
+    from ragged_blocked_kv_splitfuse_amd.runtime import PagedKVCache, num_cus
+
+    cfg = WORKLOADS[args.workload]
+    w = wl.make(cfg, args.seed)
+    init_states = w.fresh_states()
+    free_ids = np.asarray(w.free_ids, np.int32)
+    if cfg == 4:
+        # pass k of the chunked prompt: the first 512k positions are already cached
+        k = args.chunk_pass
+        c = 512 * k
+        nb = -(-c // w.block_size)
+        order = np.concatenate([w.free_ids, []]).astype(np.int32)
+        init_states[0].n_cached = c
+        init_states[0].blocks = order[:nb].tolist()
+        free_ids = order[nb:]
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    cache = PagedKVCache(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype,
+                         free_ids=free_ids)
+    wl.fill_pools_device(cache.k_pool, cache.v_pool, seed=w.seed * 7919 + 1,
+                         value_scale=w.value_scale)
+    ss = fg.SeqStates(init_states, w.table_width)
+    template = (bytes(ss.arr), ss.blocks.copy())
+    hb = fg.HostBatch(ss.n, w.table_width)
+    return dict(w=w, cache=cache, ss=ss, template=template, hb=hb, free_ids=free_ids,
+                cus=num_cus(), tdt=tdt)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path; the pass shards by KV head or by sequence with no exchange "
+              "inside it, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from ragged_blocked_kv_splitfuse_amd import fg
+    from ragged_blocked_kv_splitfuse_amd.runtime import DeviceDescriptors, Workspace, stream_handle
+
+    torch.cuda.set_device(0)
+    S = setup(args)
+    w, cache, ss, hb = S["w"], S["cache"], S["ss"], S["hb"]
+    arr_bytes, blocks0 = S["template"]
+    free_ids = S["free_ids"]
+    desc = DeviceDescriptors(ring=4)
+    ws = Workspace()
+    stream = torch.cuda.current_stream()
+    sh = stream_handle(stream)
+    kptr, vptr = cache.k_pool.data_ptr(), cache.v_pool.data_ptr()
+
+    def compose_and_plan():
+        ctypes.memmove(ctypes.addressof(ss.arr), arr_bytes, len(arr_bytes))
+        np.copyto(ss.blocks, blocks0)
+        h = fg.fg_blocked_cache_init(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                                     w.dtype, kptr, vptr, free_ids)
+        st = fg.fg_splitfuse_compose(h, ss, w.budget, hb)
+        assert st == fg.FG_OK
+        info, work = fg.fg_attention_plan(h, hb, w.num_q_heads, S["cus"])
+        return h, info, work
+
+    # pass shape and inputs
+    h, info, work = compose_and_plan()
+    T, nseq = hb.num_tokens, hb.num_seqs
+    ctx = hb.context_len[:nseq].astype(np.int64)
+    nq = hb.n_query[:nseq].astype(np.int64)
+    fg.fg_blocked_cache_destroy(h)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed * 104729 + 17)
+    mk = lambda heads: (torch.randn((T, heads, w.head_dim), generator=g, device="cuda")
+                        * w.value_scale).to(S["tdt"])
+    q, k_new, v_new = mk(w.num_q_heads), mk(w.num_kv_heads), mk(w.num_kv_heads)
+    out = torch.empty((T, w.num_q_heads, w.head_dim), dtype=S["tdt"], device="cuda")
+    wptr, wbytes = ws.ensure(max(info.workspace_bytes, 1 << 20))
+
+    e = 2 if w.dtype == "bf16" else 4
+    kv_tokens = int((ctx + nq).sum())
+    attn_bytes = kv_tokens * w.num_kv_heads * w.head_dim * e * 2 + 2 * T * w.num_q_heads * w.head_dim * e
+    pairs = int((nq * ctx + nq * (nq + 1) // 2).sum())
+    attn_flops = 4 * w.head_dim * w.num_q_heads * pairs
+    append_bytes = 4 * T * w.num_kv_heads * w.head_dim * e
+
+    n_total = args.warmup + args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(n_total)]
+    host_s = []
+
+    def step(i):
+        t0 = time.perf_counter()
+        h, info, work = compose_and_plan()
+        c = desc.upload(hb, work, stream)
+        ev[i][0].record(stream)
+        fg.fg_kv_append(h, c, k_new.data_ptr(), v_new.data_ptr(), sh)
+        ev[i][1].record(stream)
+        fg.fg_ragged_attention(h, c, info, desc.work_ptr, q.data_ptr(), w.num_q_heads, w.scale,
+                               out.data_ptr(), wptr, wbytes, sh)
+        ev[i][2].record(stream)
+        fg.fg_blocked_cache_destroy(h)
+        host_s.append(time.perf_counter() - t0)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_total):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    timed = ev[args.warmup:]
+    attn_ms = [a.elapsed_time(b2) for _, a, b2 in timed]   # attention launch only
+    app_ms = [a0.elapsed_time(a) for a0, a, _ in timed]
+    t_attn = float(np.mean(attn_ms)) * 1e-3
+    t_app = float(np.mean(app_ms)) * 1e-3
+    elapsed = t1 - t0
+    value = T * args.steps / elapsed
+
+    if w.dtype == "bf16" and args.workload != "chunked":
+        roof = {"bound": "hbm", "achieved": attn_bytes / t_attn / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    elif w.dtype == "bf16":
+        roof = {"bound": "mfma", "achieved": attn_flops / t_attn / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "alu", "achieved": attn_flops / t_attn / 1e12,
+                "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        rec = tr.get(args.workload)
+        if rec and rec.get("kernel_source") == kernel_source_hash():
+            roof["traffic"] = rec["bytes_per_launch"]
+    roof["kernel"] = "attention_bf16_kernel" if w.dtype == "bf16" else "attention_f32_kernel"
+    roof["algorithmic_bytes"] = attn_bytes
+    roof["algorithmic_flops"] = attn_flops
+    roof["mfma_frac"] = attn_flops / t_attn / 1e12 / BF16_PEAK_TFLOPS
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size, "token_budget": w.budget,
+                   "num_seqs": nseq, "tokens": T, "kv_tokens": kv_tokens,
+                   "decode_seqs": int((nq == 1).sum()), "work_records": int(info.num_work),
+                   "split_groups": int(info.num_groups)},
+        "roofline": roof,
+        "kernels": {"attention_us": t_attn * 1e6, "kv_append_us": t_app * 1e6,
+                    "kv_append_GBps": append_bytes / t_app / 1e9,
+                    "gpu_only_tokens_per_s": T / (t_attn + t_app),
+                    "host_us_per_step": float(np.mean(host_s[args.warmup:])) * 1e6},
+        "cpu_baseline": cpu_baseline(args, w, cache, hb, q, k_new, v_new) if args.cpu_seconds > 0 else None,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, w, cache, hb, q, k_new, v_new):
+    """The oracle, as it stands, on a bounded sample of the same pass: all sequences and
+    tokens, a subset of KV heads (work is linear in heads), scaled to the full pass."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from oracle.compose import OracleBatch
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    S = hb.num_seqs
+    batch = OracleBatch(hb.query_start[:S + 1].copy(), hb.n_query[:S].copy(),
+                        hb.context_len[:S].copy(), hb.block_table[:S].copy(),
+                        hb.seq_index[:S].copy(), hb.seq_id[:S].copy())
+    G = w.num_q_heads // w.num_kv_heads
+    bits = (lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)) if w.dtype == "bf16" \
+        else (lambda t: t.cpu().numpy())
+
+    def run(hk):
+        kp = bits(cache.k_pool[:, :hk].contiguous())
+        vp = bits(cache.v_pool[:, :hk].contiguous())
+        qq = bits(q[:, :hk * G].contiguous())
+        kn = bits(k_new[:, :hk].contiguous())
+        vn = bits(v_new[:, :hk].contiguous())
+        t0 = time.perf_counter()
+        oracle.kv_append(kp, vp, kn, vn, batch, w.block_size)
+        oracle.ragged_attention(qq, kp, vp, batch, hk * G, hk, w.scale, w.block_size, w.dtype)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    hk = int(min(w.num_kv_heads, max(1, args.cpu_seconds // max(t1, 1e-3))))
+    t = run(hk) if hk > 1 else t1
+    full = t * w.num_kv_heads / hk
+    return {"value": hb.num_tokens / full, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"numpy fp64 oracle (append + attention) on {hk} of {w.num_kv_heads} KV "
+                      f"heads of the same pass (all {S} sequences, {hb.num_tokens} tokens), "
+                      f"{t:.1f} s, scaled x{w.num_kv_heads / hk:g} to the full pass"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * fg.h — C ABI of the fixed-budget ragged pass over a blocked KV cache (MI355X / gfx950).
+ *
+ * One pass of the method, as the pages describe it:
+ *   - Dynamic SplitFuse composition (DeepSpeed-FastGen paper card by Holmes et al. 2024,
+ *     "Summary" and "Interesting ideas"): every forward pass runs a fixed token budget;
+ *     long prompts are cut into chunks spread over passes, generation tokens and short
+ *     prompts are packed in to fill the budget exactly;          -> fg_splitfuse_compose
+ *   - the blocked (paged) KV cache it builds on (same card, "Key points", PagedAttention):
+ *     physical blocks named by per-sequence block tables;        -> fg_blocked_cache_init,
+ *                                                                   fg_kv_append
+ *   - exact causal attention of every new token over its sequence's whole cached history
+ *     (same card, "Key points" and "References": FlashAttention-derived kernels, an exact
+ *     attention);                                                 -> fg_ragged_attention
+ *
+ * Conventions (all functions):
+ *   - Plain pointers and sizes only.  "host" pointers are CPU memory; "device" pointers are
+ *     GPU memory (hipMalloc / torch CUDA tensors).  The caller owns ALL memory: pools, Q,
+ *     new K/V, outputs, device copies of descriptors, the work list and the workspace.  The
+ *     library owns only the opaque fg_cache handle and its free list (host memory).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
+ *     enqueued asynchronously on it; no call allocates device memory or synchronises.
+ *   - Every function returns fg_status and never aborts or throws across the ABI.  On an
+ *     error nothing is launched and no state is changed, unless stated otherwise;
+ *     fg_last_error() returns a thread-local message for the last failing call.
+ *   - Asynchronous device faults surface at the caller's next synchronisation.
+ *   - A handle is not thread-safe; use one per thread or lock around it.
+ *
+ * Data layouts (element type = the cache dtype everywhere: float or bfloat16 bits):
+ *   q, out        [T][Hq][D]        T = batch num_tokens, rows in batch order
+ *   k_new, v_new  [T][Hkv][D]
+ *   K pool        [num_blocks][Hkv][block_size][D]   key-major inside a block
+ *   V pool        [num_blocks][Hkv][D][block_size]   feature-major inside a block
+ * The V pool keeps each block feature-major so that the P.V contraction, which runs over
+ * keys, reads keys contiguously; the K pool keeps keys major so that Q.K^T, which runs over
+ * the head dimension, reads D contiguously.  Query head g uses KV head g / (Hq / Hkv).
+ */
+#ifndef FG_H
+#define FG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fg_status {
+  FG_OK = 0,
+  FG_E_ARG = 1,          /* bad argument: null pointer, size out of range, capacity too small */
+  FG_E_DESC = 2,         /* descriptor validation failed (block ids, counts, capacity) */
+  FG_E_NO_BLOCKS = 3,    /* composition: there was demand but the pool could not take a token */
+  FG_E_UNSUPPORTED = 4,  /* shape or dtype the kernels do not implement */
+  FG_E_HIP = 5,          /* a HIP launch reported an error */
+  FG_E_WORKSPACE = 6     /* workspace missing or smaller than fg_attention_plan asked for */
+} fg_status;
+
+typedef enum fg_dtype { FG_F32 = 0, FG_BF16 = 1 } fg_dtype;
+
+/* Number of int32 per work-list record produced by fg_attention_plan. */
+#define FG_WORK_INTS 12
+
+typedef struct fg_cache fg_cache; /* opaque, host-side */
+
+typedef struct fg_cache_config {
+  int32_t num_blocks;   /* physical blocks in each pool, >= 1 */
+  int32_t block_size;   /* tokens per block: power of two in [1, 1024]; bf16 attention
+                           needs >= 8 */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;     /* D: 64 or 128 for FG_F32; 128 for FG_BF16 */
+  int32_t dtype;        /* fg_dtype of pools, q, k_new, v_new and out */
+} fg_cache_config;
+
+/* One request as the scheduler sees it (host memory, caller-owned). */
+typedef struct fg_seq_state {
+  int64_t seq_id;      /* caller's id, copied into the batch */
+  int32_t n_cached;    /* tokens whose K/V are already in the cache */
+  int32_t prompt_len;  /* n_cached < prompt_len: prompt phase; otherwise one decode token */
+  int32_t n_blocks;    /* blocks owned so far (in/out) */
+  int32_t max_blocks;  /* capacity of blocks[]; the sequence never owns more */
+  int32_t *blocks;     /* physical ids in logical order (in/out), capacity max_blocks */
+  int32_t n_scheduled; /* out: tokens given to this sequence in the composed pass */
+  int32_t reserved;
+} fg_seq_state;
+
+/* Ragged batch descriptor.  The struct itself is always host memory; its arrays are host
+ * memory for fg_splitfuse_compose / fg_attention_plan / fg_validate_batch and device memory
+ * (a copy the caller made) for fg_kv_append / fg_ragged_attention. */
+typedef struct fg_ragged_batch {
+  int32_t num_seqs;     /* S: sequences in the pass */
+  int32_t num_tokens;   /* T = sum of n_query */
+  int32_t table_stride; /* int32 per block_table row */
+  int32_t seq_capacity; /* compose output: capacity of the per-sequence arrays */
+  int32_t *query_start; /* [S+1] prefix sums of n_query (first row of each sequence) */
+  int32_t *n_query;     /* [S] new tokens of each sequence in this pass, >= 1 */
+  int32_t *context_len; /* [S] tokens cached BEFORE this pass */
+  int32_t *block_table; /* [S][table_stride] physical ids, -1 padded */
+  int32_t *seq_index;   /* [S] index into the fg_seq_state array given to compose */
+  int64_t *seq_id;      /* [S] */
+} fg_ragged_batch;
+
+typedef struct fg_attention_plan_info {
+  int32_t num_work;          /* work records needed (written if capacity allowed) */
+  int32_t num_groups;        /* key-range split groups */
+  int64_t workspace_bytes;   /* device workspace fg_ragged_attention needs (0: none) */
+  int64_t counter_bytes;     /* leading part of the workspace holding split counters */
+  int32_t num_q_heads;       /* Hq the plan was made for */
+  int32_t num_tokens;        /* T of the batch the plan was made for */
+} fg_attention_plan_info;
+
+/* ---- cache handle and block allocator ------------------------------------------------ */
+
+/* Creates the host handle of a blocked KV cache whose two pools the caller allocated
+ * (device memory, layouts above; sizes num_blocks*Hkv*block_size*D elements each).
+ * free_ids[0..n_free) are the physical ids the allocator may hand out, in the order they
+ * are handed out (ids already owned by sequences must not be listed); free_ids may be NULL
+ * with n_free = -1 to mean 0..num_blocks-1 in order.  The free list is a stack: released
+ * ids are handed out next, the last released first.
+ * Errors: FG_E_ARG (null out/cfg, sizes out of range, an id out of range or repeated),
+ * FG_E_UNSUPPORTED (block_size/head_dim/dtype combination not implemented). */
+fg_status fg_blocked_cache_init(const fg_cache_config *cfg, void *k_pool, void *v_pool,
+                                const int32_t *free_ids, int32_t n_free, fg_cache **out);
+fg_status fg_blocked_cache_destroy(fg_cache *cache);
+int32_t fg_blocked_cache_num_free(const fg_cache *cache); /* -1 on a null handle */
+/* Copies the free ids in hand-out order into out[0..cap); *n_out = number of free ids. */
+fg_status fg_blocked_cache_free_ids(const fg_cache *cache, int32_t *out, int32_t cap,
+                                    int32_t *n_out);
+/* Returns blocks of a finished sequence to the free list.  FG_E_ARG if an id is out of
+ * range or already free (then nothing is released). */
+fg_status fg_blocked_cache_release(fg_cache *cache, const int32_t *blocks, int32_t n);
+
+/* ---- Dynamic SplitFuse composition (host) -------------------------------------------- */
+
+/* Composes one pass of at most token_budget tokens over seqs[0..n_seqs):
+ *   1. each sequence in its generation phase (n_cached >= prompt_len) gets 1 token, in
+ *      array order;
+ *   2. prompt tokens fill what is left, sequences in array (arrival) order, the last one cut
+ *      so the budget is filled exactly when demand allows; a shorter pass is not padded.
+ * Before a sequence gets n tokens it is given blocks up to ceil((n_cached+n)/block_size)
+ * from the free list; if the pool runs dry it gets what fits (a decode: 0 or 1 token).
+ * Writes the batch (sequences with n_scheduled > 0, in array order) into out's host
+ * arrays, which need out->seq_capacity >= n_seqs and out->table_stride >= every
+ * max_blocks.  Mutates seqs[i].blocks/n_blocks/n_scheduled and the free list only.
+ * Errors: FG_E_ARG (budget < 1, null pointers, capacities), FG_E_NO_BLOCKS (demand, but
+ * not a single token fitted; the batch is empty and nothing changed). */
+fg_status fg_splitfuse_compose(fg_cache *cache, fg_seq_state *seqs, int32_t n_seqs,
+                               int32_t token_budget, fg_ragged_batch *out);
+/* After the pass ran: n_cached += n_scheduled, n_scheduled = 0, for every sequence. */
+fg_status fg_splitfuse_commit(fg_seq_state *seqs, int32_t n_seqs);
+
+/* Full O(S * table_stride) check of a host batch: prefix sums, n_query >= 1, every block a
+ * valid id, no id used twice, enough blocks for context_len + n_query.  FG_E_DESC names the
+ * first violation in fg_last_error(). */
+fg_status fg_validate_batch(const fg_cache *cache, const fg_ragged_batch *host);
+
+/* ---- device work -------------------------------------------------------------------- */
+
+/* Appends the pass's new rows: new token i of sequence s (position context_len[s]+i) goes
+ * to block block_table[s][pos / block_size], slot pos % block_size, of both pools.  A bit
+ * copy; no other element of either pool is written.  `dev` arrays are device memory.
+ * k_new, v_new: device [T][Hkv][D].  Errors: FG_E_ARG, FG_E_HIP. */
+fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const void *k_new,
+                       const void *v_new, void *stream);
+
+/* Splits the attention of a host batch into work records for one launch (host only).
+ * Sequences with few query rows become key-streaming records, chunk rows become 128-row
+ * tiles, and long key ranges are split so about num_cus * 4 records exist; records come
+ * longest first.  Writes min(num_work, work_capacity) records of FG_WORK_INTS int32 into
+ * `work` (host) and fills *info; returns FG_E_ARG when work_capacity < num_work (call
+ * with capacity 0 to size).  The caller copies `work` to the device. */
+fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *host,
+                            int32_t num_q_heads, int32_t num_cus,
+                            fg_attention_plan_info *info, int32_t *work,
+                            int32_t work_capacity);
+
+/* Exact causal attention of every new token over its sequence's cached history (keys
+ * 0 .. context_len[s] + i for new token i, which includes the rows fg_kv_append just
+ * wrote): out[t][g] = sum_j softmax_j(scale * q[t][g] . K_j) V_j.  bf16 inputs: products
+ * on bf16 MFMA with fp32 accumulation, output rounded to nearest even; fp32 inputs: fp32
+ * arithmetic.  `dev` arrays, q, out, work_dev and workspace are device memory; `plan` is
+ * the host info fg_attention_plan returned for this batch and work_dev the device copy of
+ * its records (both unused for FG_F32).  The first plan->counter_bytes of the workspace
+ * must be zero before the first call that uses it (each call leaves them zero again);
+ * calls sharing a workspace must be ordered on one stream.
+ * Errors: FG_E_ARG, FG_E_UNSUPPORTED, FG_E_WORKSPACE, FG_E_HIP. */
+fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
+                              const fg_attention_plan_info *plan, const int32_t *work_dev,
+                              const void *q, int32_t num_q_heads, float scale, void *out,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- diagnostics -------------------------------------------------------------------- */
+const char *fg_status_string(fg_status status);
+const char *fg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FG_H */

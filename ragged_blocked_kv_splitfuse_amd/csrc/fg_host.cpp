@@ -1,0 +1,418 @@
+// Host side of the library: block allocator, Dynamic SplitFuse composition, descriptor
+// validation and the attention work-list planner.  No HIP runtime calls, so it builds with a
+// plain C++ compiler and runs on machines without a GPU.
+//
+// Composition follows DeepSpeed-FastGen paper card by Holmes et al. (2024), "Summary" and
+// "Interesting ideas" (fixed token budget per pass; long prompts cut into chunks over several
+// passes; short prompts and generation tokens packed to fill the budget exactly), the reading
+// notes page on DeepSpeed-FastGen, method paragraph (each request split into prompt and
+// generation work), and the blog's "1. Introduction" (generation must not be stalled by
+// prompt processing).  The blocked cache is the PagedAttention-style cache named in the
+// card's "Key points".
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "fg_internal.h"
+
+namespace fgi {
+
+static thread_local char g_err[512] = "";
+
+fg_status fail(fg_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == FG_BF16 ? 2 : 4; }
+
+}  // namespace fgi
+
+using namespace fgi;
+
+extern "C" {
+
+const char *fg_last_error(void) { return g_err; }
+
+const char *fg_status_string(fg_status st) {
+  switch (st) {
+    case FG_OK: return "ok";
+    case FG_E_ARG: return "invalid argument";
+    case FG_E_DESC: return "invalid batch descriptor";
+    case FG_E_NO_BLOCKS: return "no free blocks";
+    case FG_E_UNSUPPORTED: return "unsupported shape or dtype";
+    case FG_E_HIP: return "HIP error";
+    case FG_E_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+// --------------------------------------------------------------------------------------
+// cache handle and allocator
+// --------------------------------------------------------------------------------------
+
+fg_status fg_blocked_cache_init(const fg_cache_config *cfg, void *k_pool, void *v_pool,
+                                const int32_t *free_ids, int32_t n_free, fg_cache **out) {
+  clear_error();
+  if (!cfg || !out) return fail(FG_E_ARG, "cfg and out must not be null");
+  *out = nullptr;
+  const fg_cache_config c = *cfg;
+  if (c.num_blocks < 1) return fail(FG_E_ARG, "num_blocks must be >= 1 (got %d)", c.num_blocks);
+  if (c.block_size < 1 || c.block_size > 1024 || (c.block_size & (c.block_size - 1)))
+    return fail(FG_E_UNSUPPORTED, "block_size must be a power of two in [1, 1024] (got %d)",
+                c.block_size);
+  if (c.num_kv_heads < 1) return fail(FG_E_ARG, "num_kv_heads must be >= 1");
+  if (c.dtype != FG_F32 && c.dtype != FG_BF16) return fail(FG_E_ARG, "unknown dtype %d", c.dtype);
+  if (c.dtype == FG_BF16 && c.head_dim != 128)
+    return fail(FG_E_UNSUPPORTED, "bf16 kernels implement head_dim 128 (got %d)", c.head_dim);
+  if (c.dtype == FG_F32 && c.head_dim != 64 && c.head_dim != 128)
+    return fail(FG_E_UNSUPPORTED, "fp32 kernels implement head_dim 64 or 128 (got %d)",
+                c.head_dim);
+  std::vector<int32_t> ids;
+  if (n_free < 0) {
+    if (free_ids) return fail(FG_E_ARG, "n_free < 0 requires free_ids == NULL");
+    ids.resize(c.num_blocks);
+    for (int32_t i = 0; i < c.num_blocks; ++i) ids[i] = i;
+  } else {
+    if (n_free > 0 && !free_ids) return fail(FG_E_ARG, "free_ids is null");
+    ids.assign(free_ids, free_ids + n_free);
+  }
+  std::vector<uint8_t> is_free(c.num_blocks, 0);
+  for (int32_t b : ids) {
+    if (b < 0 || b >= c.num_blocks) return fail(FG_E_ARG, "free id %d out of range", b);
+    if (is_free[b]) return fail(FG_E_ARG, "free id %d listed twice", b);
+    is_free[b] = 1;
+  }
+  fg_cache *h = new (std::nothrow) fg_cache();
+  if (!h) return fail(FG_E_ARG, "out of host memory");
+  h->cfg = c;
+  h->k_pool = k_pool;
+  h->v_pool = v_pool;
+  h->bs_log2 = 0;
+  while ((1 << h->bs_log2) < c.block_size) ++h->bs_log2;
+  h->free_stack.assign(ids.rbegin(), ids.rend());  // ids[0] ends on top
+  h->is_free = std::move(is_free);
+  *out = h;
+  return FG_OK;
+}
+
+fg_status fg_blocked_cache_destroy(fg_cache *cache) {
+  clear_error();
+  delete cache;
+  return FG_OK;
+}
+
+int32_t fg_blocked_cache_num_free(const fg_cache *cache) {
+  return cache ? (int32_t)cache->free_stack.size() : -1;
+}
+
+fg_status fg_blocked_cache_free_ids(const fg_cache *cache, int32_t *out, int32_t cap,
+                                    int32_t *n_out) {
+  clear_error();
+  if (!cache || !n_out) return fail(FG_E_ARG, "null argument");
+  const int32_t n = (int32_t)cache->free_stack.size();
+  *n_out = n;
+  if (cap > 0 && !out) return fail(FG_E_ARG, "out is null");
+  for (int32_t i = 0; i < std::min(n, cap); ++i) out[i] = cache->free_stack[n - 1 - i];
+  return FG_OK;
+}
+
+fg_status fg_blocked_cache_release(fg_cache *cache, const int32_t *blocks, int32_t n) {
+  clear_error();
+  if (!cache) return fail(FG_E_ARG, "null cache");
+  if (n < 0 || (n > 0 && !blocks)) return fail(FG_E_ARG, "bad block list");
+  std::vector<uint8_t> seen(cache->cfg.num_blocks, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = blocks[i];
+    if (b < 0 || b >= cache->cfg.num_blocks) return fail(FG_E_ARG, "block %d out of range", b);
+    if (cache->is_free[b] || seen[b]) return fail(FG_E_ARG, "block %d is already free", b);
+    seen[b] = 1;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    cache->free_stack.push_back(blocks[i]);
+    cache->is_free[blocks[i]] = 1;
+  }
+  return FG_OK;
+}
+
+// --------------------------------------------------------------------------------------
+// Dynamic SplitFuse composition
+// --------------------------------------------------------------------------------------
+
+// Tokens sequence `s` can take (<= want); pops the blocks they need from the free list.
+static int32_t grant(fg_cache *cache, fg_seq_state &s, int32_t want) {
+  const int32_t bs = cache->cfg.block_size;
+  const int64_t c = s.n_cached;
+  want = (int32_t)std::min<int64_t>(want, (int64_t)s.max_blocks * bs - c);
+  if (want <= 0) return 0;
+  const int64_t need_blocks = (c + want + bs - 1) / bs;
+  int64_t missing = need_blocks - s.n_blocks;
+  const int64_t avail = (int64_t)cache->free_stack.size();
+  if (missing > avail) {
+    want = (int32_t)(((int64_t)s.n_blocks + avail) * bs - c);
+    missing = avail;
+    if (want <= 0) return 0;
+  }
+  for (int64_t i = 0; i < missing; ++i) {
+    const int32_t b = cache->free_stack.back();
+    cache->free_stack.pop_back();
+    cache->is_free[b] = 0;
+    s.blocks[s.n_blocks++] = b;
+  }
+  return want;
+}
+
+fg_status fg_splitfuse_compose(fg_cache *cache, fg_seq_state *seqs, int32_t n_seqs,
+                               int32_t token_budget, fg_ragged_batch *out) {
+  clear_error();
+  if (!cache || !out) return fail(FG_E_ARG, "null cache or batch");
+  if (n_seqs < 0 || (n_seqs > 0 && !seqs)) return fail(FG_E_ARG, "bad sequence array");
+  if (token_budget < 1) return fail(FG_E_ARG, "token budget must be >= 1 (got %d)", token_budget);
+  if (out->seq_capacity < n_seqs)
+    return fail(FG_E_ARG, "batch seq_capacity %d < n_seqs %d", out->seq_capacity, n_seqs);
+  if (!out->query_start || (n_seqs > 0 && (!out->n_query || !out->context_len ||
+                                           !out->block_table || !out->seq_index || !out->seq_id)))
+    return fail(FG_E_ARG, "batch arrays must not be null");
+  const int32_t bs = cache->cfg.block_size;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const fg_seq_state &s = seqs[i];
+    if (s.n_cached < 0 || s.prompt_len < 0 || s.n_blocks < 0 || s.max_blocks < 0 ||
+        s.n_blocks > s.max_blocks || (s.max_blocks > 0 && !s.blocks))
+      return fail(FG_E_ARG, "sequence %d: inconsistent state", i);
+    if ((int64_t)s.n_blocks * bs < s.n_cached)
+      return fail(FG_E_ARG, "sequence %d: %d blocks cannot hold %d cached tokens", i,
+                  s.n_blocks, s.n_cached);
+    if (s.max_blocks > out->table_stride)
+      return fail(FG_E_ARG, "sequence %d: max_blocks %d > table_stride %d", i, s.max_blocks,
+                  out->table_stride);
+  }
+  for (int32_t i = 0; i < n_seqs; ++i) seqs[i].n_scheduled = 0;
+  int32_t left = token_budget;
+  // generation tokens first: one per decoding sequence, array order
+  for (int32_t i = 0; i < n_seqs && left > 0; ++i) {
+    fg_seq_state &s = seqs[i];
+    if (s.n_cached >= s.prompt_len) {
+      const int32_t n = grant(cache, s, 1);
+      s.n_scheduled = n;
+      left -= n;
+    }
+  }
+  // then prompt tokens, arrival order; the last one is cut to fill the budget
+  for (int32_t i = 0; i < n_seqs && left > 0; ++i) {
+    fg_seq_state &s = seqs[i];
+    if (s.n_cached < s.prompt_len) {
+      const int32_t n = grant(cache, s, std::min(s.prompt_len - s.n_cached, left));
+      s.n_scheduled = n;
+      left -= n;
+    }
+  }
+  int32_t S = 0;
+  out->query_start[0] = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const fg_seq_state &s = seqs[i];
+    if (s.n_scheduled <= 0) continue;
+    out->n_query[S] = s.n_scheduled;
+    out->query_start[S + 1] = out->query_start[S] + s.n_scheduled;
+    out->context_len[S] = s.n_cached;
+    int32_t *row = out->block_table + (size_t)S * out->table_stride;
+    for (int32_t k = 0; k < out->table_stride; ++k) row[k] = k < s.n_blocks ? s.blocks[k] : -1;
+    out->seq_index[S] = i;
+    out->seq_id[S] = s.seq_id;
+    ++S;
+  }
+  out->num_seqs = S;
+  out->num_tokens = out->query_start[S];
+  if (S == 0 && n_seqs > 0)
+    return fail(FG_E_NO_BLOCKS, "no sequence could be given a token: the block pool is empty");
+  return FG_OK;
+}
+
+fg_status fg_splitfuse_commit(fg_seq_state *seqs, int32_t n_seqs) {
+  clear_error();
+  if (n_seqs < 0 || (n_seqs > 0 && !seqs)) return fail(FG_E_ARG, "bad sequence array");
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    seqs[i].n_cached += seqs[i].n_scheduled;
+    seqs[i].n_scheduled = 0;
+  }
+  return FG_OK;
+}
+
+// --------------------------------------------------------------------------------------
+// validation
+// --------------------------------------------------------------------------------------
+
+fg_status fg_validate_batch(const fg_cache *cache, const fg_ragged_batch *b) {
+  clear_error();
+  if (!cache || !b) return fail(FG_E_ARG, "null argument");
+  const int32_t S = b->num_seqs, bs = cache->cfg.block_size, NB = cache->cfg.num_blocks;
+  if (S < 0 || b->num_tokens < 0 || b->table_stride < 0) return fail(FG_E_DESC, "negative size");
+  if (!b->query_start) return fail(FG_E_DESC, "query_start is null");
+  if (S > 0 && (!b->n_query || !b->context_len || !b->block_table))
+    return fail(FG_E_DESC, "descriptor arrays are null");
+  if (b->query_start[0] != 0) return fail(FG_E_DESC, "query_start[0] = %d", b->query_start[0]);
+  std::vector<int32_t> owner(NB, -1);
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t n = b->n_query[s], c = b->context_len[s];
+    if (n < 1) return fail(FG_E_DESC, "sequence %d has n_query %d", s, n);
+    if (c < 0) return fail(FG_E_DESC, "sequence %d has context_len %d", s, c);
+    if ((int64_t)b->query_start[s + 1] != (int64_t)b->query_start[s] + n)
+      return fail(FG_E_DESC, "query_start[%d] is not the prefix sum", s + 1);
+    const int64_t need = ((int64_t)c + n + bs - 1) / bs;
+    if (need > b->table_stride)
+      return fail(FG_E_DESC, "sequence %d needs %lld blocks, table_stride %d", s,
+                  (long long)need, b->table_stride);
+    const int32_t *row = b->block_table + (size_t)s * b->table_stride;
+    for (int64_t k = 0; k < b->table_stride; ++k) {
+      const int32_t id = row[k];
+      if (k < need && id < 0) return fail(FG_E_DESC, "sequence %d: block %lld missing", s, (long long)k);
+      if (id < 0) continue;
+      if (id >= NB) return fail(FG_E_DESC, "sequence %d: block id %d out of range", s, id);
+      if (owner[id] >= 0)
+        return fail(FG_E_DESC, "block %d used by sequences %d and %d", id, owner[id], s);
+      owner[id] = s;
+    }
+  }
+  if (b->query_start[S] != b->num_tokens)
+    return fail(FG_E_DESC, "num_tokens %d != sum of n_query %d", b->num_tokens, b->query_start[S]);
+  return FG_OK;
+}
+
+// --------------------------------------------------------------------------------------
+// attention work list
+// --------------------------------------------------------------------------------------
+
+namespace {
+struct PlanItem {
+  int32_t s, h, tok0, ntok, klo, khi, mode;
+  int32_t group, split, nsplit;
+  int64_t poff;
+  double cost;
+  int64_t order;
+};
+}  // namespace
+
+fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
+                            int32_t num_q_heads, int32_t num_cus, fg_attention_plan_info *info,
+                            int32_t *work, int32_t work_capacity) {
+  clear_error();
+  if (!cache || !b || !info) return fail(FG_E_ARG, "null argument");
+  std::memset(info, 0, sizeof(*info));
+  const int32_t Hkv = cache->cfg.num_kv_heads, D = cache->cfg.head_dim;
+  if (num_q_heads < 1 || num_q_heads % Hkv)
+    return fail(FG_E_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, Hkv);
+  const int32_t G = num_q_heads / Hkv;
+  if (G > TILE_ROWS) return fail(FG_E_UNSUPPORTED, "more than %d query heads per KV head", TILE_ROWS);
+  if (num_cus < 1) return fail(FG_E_ARG, "num_cus must be >= 1");
+  if (b->num_seqs < 0 || (b->num_seqs > 0 && (!b->n_query || !b->context_len || !b->query_start)))
+    return fail(FG_E_ARG, "bad batch");
+  info->num_q_heads = num_q_heads;
+  info->num_tokens = b->num_tokens;
+  if (cache->cfg.dtype == FG_F32) return FG_OK;  // the fp32 kernel needs no work list
+
+  const double e = elem_bytes(cache->cfg.dtype);
+  // Cost in "HBM-byte equivalents": a streamed record moves 2*D*e bytes per key; a tile
+  // record does 4*D flops per visible (row, key) pair, converted at 8 TB/s against half the
+  // bf16 MFMA peak, plus its K/V reads (mostly L2 hits, weighted down).
+  const double flop_to_byte = 8.0e12 / (0.5 * 2.5e15);
+  std::vector<PlanItem> base;
+  for (int32_t s = 0; s < b->num_seqs; ++s) {
+    const int32_t c = b->context_len[s], n = b->n_query[s];
+    if (n < 1 || c < 0) return fail(FG_E_DESC, "sequence %d: n_query %d, context_len %d", s, n, c);
+    const int32_t tpt = (n * G <= STREAM_ROWS) ? n : TILE_ROWS / G;
+    for (int32_t t0 = 0; t0 < n; t0 += tpt) {
+      const int32_t nt = std::min(tpt, n - t0);
+      const int32_t mode = nt * G <= STREAM_ROWS ? MODE_STREAM : MODE_TILE;
+      const int32_t keys = c + t0 + nt;
+      double cost;
+      if (mode == MODE_STREAM) {
+        cost = (double)keys * 2.0 * D * e;
+      } else {
+        const double pairs = (double)G * ((double)nt * (c + t0) + 0.5 * nt * (nt + 1));
+        cost = pairs * 4.0 * D * flop_to_byte + 0.25 * keys * 2.0 * D * e;
+      }
+      for (int32_t h = 0; h < Hkv; ++h)
+        base.push_back({s, h, t0, nt, 0, keys, mode, -1, 0, 1, 0, cost, (int64_t)base.size()});
+    }
+  }
+  double total = 0;
+  for (auto &it : base) total += it.cost;
+  const double target = total / (4.0 * num_cus);
+  const int32_t min_tiles = 4;  // a split covers at least 4 key tiles (256 keys)
+
+  std::vector<PlanItem> items;
+  int32_t groups = 0;
+  int64_t poff_bytes = 0;  // partial storage, bytes after the counters
+  for (auto &it : base) {
+    const int32_t tiles = (it.khi + KEY_TILE - 1) / KEY_TILE;
+    int32_t nsplit = 1;
+    if (target > 0 && it.cost > target) nsplit = (int32_t)std::ceil(it.cost / target);
+    nsplit = std::max(1, std::min(nsplit, tiles / min_tiles));
+    if (nsplit == 1) {
+      items.push_back(it);
+      continue;
+    }
+    const int32_t g = groups++;
+    const int64_t poff = poff_bytes;
+    poff_bytes += (int64_t)nsplit * slot_floats(it.mode, D) * 4;
+    int32_t tile = 0;
+    for (int32_t k = 0; k < nsplit; ++k) {
+      const int32_t nt = tiles / nsplit + (k < tiles % nsplit ? 1 : 0);
+      PlanItem p = it;
+      p.klo = tile * KEY_TILE;
+      p.khi = std::min(it.khi, (tile + nt) * KEY_TILE);
+      p.group = g;
+      p.split = k;
+      p.nsplit = nsplit;
+      p.poff = poff;
+      p.cost = it.cost * nt / tiles;
+      tile += nt;
+      items.push_back(p);
+    }
+  }
+  // longest first (stable), so the long-running records start early
+  std::stable_sort(items.begin(), items.end(),
+                   [](const PlanItem &a, const PlanItem &b2) { return a.cost > b2.cost; });
+
+  const int64_t counter_bytes = ((int64_t)groups * 4 + 255) / 256 * 256;
+  const int64_t ws = groups ? counter_bytes + poff_bytes : 0;
+  if ((ws / 4) > INT32_MAX) return fail(FG_E_UNSUPPORTED, "workspace beyond 8 GiB");
+  if ((int64_t)items.size() > INT32_MAX) return fail(FG_E_UNSUPPORTED, "too many work records");
+  info->num_work = (int32_t)items.size();
+  info->num_groups = groups;
+  info->counter_bytes = groups ? counter_bytes : 0;
+  info->workspace_bytes = ws;
+  if (work_capacity < info->num_work) {
+    if (work_capacity == 0) return FG_OK;  // sizing call
+    return fail(FG_E_ARG, "work capacity %d < %d records", work_capacity, info->num_work);
+  }
+  if (info->num_work > 0 && !work) return fail(FG_E_ARG, "work is null");
+  for (size_t i = 0; i < items.size(); ++i) {
+    const PlanItem &p = items[i];
+    int32_t *w = work + i * FG_WORK_INTS;
+    w[W_SEQ] = p.s;
+    w[W_KVH] = p.h;
+    w[W_TOK0] = p.tok0;
+    w[W_NTOK] = p.ntok;
+    w[W_KLO] = p.klo;
+    w[W_KHI] = p.khi;
+    w[W_MODE] = p.mode;
+    w[W_GROUP] = p.group;
+    w[W_SPLIT] = p.split;
+    w[W_NSPLIT] = p.nsplit;
+    w[W_POFF] = p.group >= 0 ? (int32_t)((counter_bytes + p.poff) / 4) : 0;
+    w[W_RES] = 0;
+  }
+  return FG_OK;
+}
+
+}  // extern "C"

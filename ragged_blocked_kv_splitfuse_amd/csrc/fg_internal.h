@@ -1,0 +1,52 @@
+// Internal declarations shared by the host library and the kernel launchers.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "fg.h"
+
+struct fg_cache {
+  fg_cache_config cfg;
+  void *k_pool;
+  void *v_pool;
+  int32_t bs_log2;
+  std::vector<int32_t> free_stack;  // top = back(); handed out from the top
+  std::vector<uint8_t> is_free;     // per physical id
+};
+
+namespace fgi {
+
+// Records written by fg_attention_plan, FG_WORK_INTS int32 each.
+enum WorkField {
+  W_SEQ = 0,    // batch index s
+  W_KVH = 1,    // KV head h
+  W_TOK0 = 2,   // first query token (index into the sequence's new tokens)
+  W_NTOK = 3,   // query tokens in the record
+  W_KLO = 4,    // first key position (multiple of KEY_TILE)
+  W_KHI = 5,    // one past the last key position the record covers
+  W_MODE = 6,   // MODE_STREAM or MODE_TILE
+  W_GROUP = 7,  // split group (counter index), -1 when the record covers its whole key range
+  W_SPLIT = 8,  // split index inside the group
+  W_NSPLIT = 9, // splits in the group
+  W_POFF = 10,  // float offset of the group's partial slot 0 inside the workspace
+  W_RES = 11
+};
+
+// MODE_STREAM: at most STREAM_ROWS query rows (decode tokens, short chunks); the four waves
+// of a workgroup take alternate key tiles and merge at the end.
+// MODE_TILE: up to TILE_ROWS query rows; all waves share every K/V tile staged in LDS.
+enum { MODE_STREAM = 0, MODE_TILE = 1 };
+constexpr int STREAM_ROWS = 16;
+constexpr int TILE_ROWS = 128;
+constexpr int KEY_TILE = 64;
+
+constexpr int64_t slot_floats(int mode, int head_dim) {
+  return (int64_t)(mode == MODE_STREAM ? STREAM_ROWS : TILE_ROWS) * (head_dim + 2);
+}
+
+fg_status fail(fg_status st, const char *fmt, ...);
+void clear_error();
+int elem_bytes(int32_t dtype);
+
+}  // namespace fgi

@@ -1,0 +1,136 @@
+"""Device-memory plumbing around the C ABI, on top of PyTorch (memory and streams only).
+
+* ``PagedKVCache``     — the two pools (torch tensors) plus the library's cache handle;
+* ``DeviceDescriptors`` — uploads a composed batch and its work list to the device in one
+  copy from a ring of pinned staging buffers (an event guards each buffer, so the host can
+  compose the next pass while the previous copy is still queued);
+* ``Workspace``         — zero-initialised device scratch for split-key partials; the kernel
+  leaves its counter region zero after every call, so it is cleared only when it grows.
+
+No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import fg
+
+TORCH_DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def num_cus(device=None) -> int:
+    return int(torch.cuda.get_device_properties(device or torch.cuda.current_device())
+               .multi_processor_count)
+
+
+def stream_handle(stream=None) -> int:
+    s = stream or torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+class PagedKVCache:
+    """Pools: K [NB][Hkv][bs][D], V [NB][Hkv][D][bs] in the cache dtype."""
+
+    def __init__(self, num_blocks, block_size, num_kv_heads, head_dim, dtype, device="cuda",
+                 free_ids=None, k_pool=None, v_pool=None):
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self.num_kv_heads, self.head_dim, self.dtype = int(num_kv_heads), int(head_dim), dtype
+        tdt = TORCH_DTYPES[dtype]
+        if k_pool is None:
+            k_pool = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=tdt,
+                                 device=device)
+        if v_pool is None:
+            v_pool = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=tdt,
+                                 device=device)
+        assert k_pool.is_contiguous() and v_pool.is_contiguous()
+        assert tuple(k_pool.shape) == (num_blocks, num_kv_heads, block_size, head_dim)
+        assert tuple(v_pool.shape) == (num_blocks, num_kv_heads, head_dim, block_size)
+        assert k_pool.dtype == tdt and v_pool.dtype == tdt
+        self.k_pool, self.v_pool = k_pool, v_pool
+        self.handle = fg.fg_blocked_cache_init(num_blocks, block_size, num_kv_heads, head_dim,
+                                               dtype, k_pool.data_ptr(), v_pool.data_ptr(),
+                                               free_ids)
+
+    def close(self):
+        if self.handle is not None:
+            fg.fg_blocked_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001  (interpreter shutdown)
+            pass
+
+
+class DeviceDescriptors:
+    """One int32 device buffer holding [query_start | n_query | context_len | block_table |
+    work records] of the current pass, and the fg_ragged_batch struct pointing into it."""
+
+    def __init__(self, device="cuda", ring: int = 3):
+        self.device = torch.device(device)
+        self.ring = [None] * ring
+        self.events = [None] * ring
+        self.slot = 0
+        self.dev = None
+        self.cstruct = fg.FgRaggedBatch()
+        self.work_ptr = 0
+
+    def _staging(self, n):
+        i = self.slot
+        self.slot = (self.slot + 1) % len(self.ring)
+        if self.events[i] is not None:
+            self.events[i].synchronize()        # the copy that last read this buffer is done
+        if self.ring[i] is None or self.ring[i].numel() < n:
+            self.ring[i] = torch.empty(max(n, 1024), dtype=torch.int32, pin_memory=True)
+        return i, self.ring[i]
+
+    def upload(self, hb: fg.HostBatch, work: np.ndarray | None = None, stream=None):
+        S, stride = hb.num_seqs, hb.table_stride
+        nw = 0 if work is None else int(work.size)
+        parts = [hb.query_start[:S + 1], hb.n_query[:S], hb.context_len[:S],
+                 hb.block_table[:S].reshape(-1)]
+        sizes = [S + 1, S, S, S * stride]
+        total = sum(sizes) + nw
+        i, host = self._staging(total)
+        h = host.numpy()
+        off = 0
+        for p, n in zip(parts, sizes):
+            h[off:off + n] = p
+            off += n
+        if nw:
+            h[off:off + nw] = work.reshape(-1)
+        if self.dev is None or self.dev.numel() < total:
+            self.dev = torch.empty(max(total, 1024), dtype=torch.int32, device=self.device)
+        s = stream or torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            self.dev[:total].copy_(host[:total], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(s)
+        self.events[i] = ev
+        base = self.dev.data_ptr()
+        offs = np.cumsum([0] + sizes)
+        p32 = lambda k: ctypes.cast(base + 4 * int(offs[k]), fg.i32p)
+        c = self.cstruct
+        c.num_seqs, c.num_tokens, c.table_stride, c.seq_capacity = S, hb.num_tokens, stride, S
+        c.query_start, c.n_query, c.context_len, c.block_table = p32(0), p32(1), p32(2), p32(3)
+        c.seq_index = None
+        c.seq_id = None
+        self.work_ptr = base + 4 * int(offs[4]) if nw else 0
+        return c
+
+
+class Workspace:
+    def __init__(self, device="cuda"):
+        self.device = torch.device(device)
+        self.buf = None
+
+    def ensure(self, nbytes: int):
+        if nbytes <= 0:
+            return 0, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(int(nbytes), dtype=torch.uint8, device=self.device)
+        return self.buf.data_ptr(), self.buf.numel()

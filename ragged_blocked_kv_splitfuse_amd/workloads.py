@@ -244,3 +244,22 @@ CONFIGS = {
 def make(config: int, seed: int | None = None, **kw) -> Workload:
     fn = CONFIGS[config]
     return fn(config if seed is None else seed, **kw)
+
+
+def fill_pools_device(k_pool, v_pool, seed: int, value_scale: float = 1.0):
+    """Fill two device pools with i.i.d. N(0, value_scale^2) values from torch's seeded
+    device generator (for passes whose cache is too large to generate on the host).
+    Every slot gets a finite value, history or not."""
+    import torch
+    g = torch.Generator(device=k_pool.device)
+    g.manual_seed(int(seed))
+    for t in (k_pool, v_pool):
+        # fill in slabs so the fp32 intermediate stays small
+        flat = t.view(t.shape[0], -1)
+        step = max(1, (1 << 27) // max(1, flat.shape[1]))
+        for i in range(0, flat.shape[0], step):
+            x = torch.randn(flat[i:i + step].shape, generator=g, device=t.device,
+                            dtype=torch.float32)
+            if value_scale != 1.0:
+                x.mul_(value_scale)
+            flat[i:i + step].copy_(x)

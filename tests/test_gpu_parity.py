@@ -1,0 +1,111 @@
+"""Parity of the HIP path (through the C ABI) with the oracle on small and mid-size passes:
+kv_append bit-exact on the whole pools, attention within the stated tolerance (bf16: max-abs
+2e-2 and mean-abs 2e-3; fp32: max-abs 1e-5).  Cases span several key tiles, ragged tails,
+both kernel modes, key-range splits, GQA/MQA groupings and block sizes."""
+import zlib
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import gpu_harness as G
+from ragged_blocked_kv_splitfuse_amd import fg, workloads as wl
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def check_append(r, w):
+    dt = np.uint16 if w.dtype == "bf16" else np.uint32
+    gk = G.to_host_bits(r["gp"].cache.k_pool, w.dtype).view(dt)
+    gv = G.to_host_bits(r["gp"].cache.v_pool, w.dtype).view(dt)
+    assert np.array_equal(gk, r["k_pool"].view(dt)), "K pool differs from the oracle's append"
+    assert np.array_equal(gv, r["v_pool"].view(dt)), "V pool differs from the oracle's append"
+
+
+def test_tiny_f32_workload():
+    w = wl.make(1)
+    r = G.full_pass(w)
+    check_append(r, w)
+    G.assert_close(G.out_to_f64(r["out"]), r["ref"], "f32", "tiny_f32")
+
+
+CASES = {
+    # name: (custom kwargs, num_cus)  -- a huge num_cus forces the finest key splits
+    "mha_mixed": (dict(hq=8, hkv=8, bs=64, budget=300, n_decode=5, decode_ctx=(1, 700),
+                       prompts=((100, 400), (0, 300))), 256),
+    "gqa4_mixed": (dict(hq=32, hkv=8, bs=64, budget=200, n_decode=6, decode_ctx=(0, 900),
+                        prompts=((70, 160), (0, 500))), 256),
+    "mha_split": (dict(hq=4, hkv=4, bs=64, budget=260, n_decode=4, decode_ctx=(1500, 3000),
+                       prompts=((1700, 2100),)), 100000),
+    "gqa4_split": (dict(hq=16, hkv=4, bs=64, budget=150, n_decode=3, decode_ctx=(1200, 2600),
+                        prompts=((2000, 2100), (0, 40))), 100000),
+    "bs16": (dict(hq=4, hkv=4, bs=16, budget=180, n_decode=3, decode_ctx=(0, 300),
+                  prompts=((37, 200),)), 256),
+    "bs8_split": (dict(hq=4, hkv=2, bs=8, budget=90, n_decode=2, decode_ctx=(300, 700),
+                       prompts=((600, 700),)), 100000),
+    "bs128": (dict(hq=8, hkv=4, bs=128, budget=160, n_decode=3, decode_ctx=(0, 500),
+                   prompts=((129, 300),)), 256),
+    "stream_chunks_gqa": (dict(hq=16, hkv=4, bs=64, budget=9, n_decode=2, decode_ctx=(5, 90),
+                               prompts=((20, 23), (0, 4))), 256),
+    "mqa_g32": (dict(hq=32, hkv=1, bs=64, budget=40, n_decode=5, decode_ctx=(0, 400),
+                     prompts=((10, 60),)), 256),
+    "gqa3": (dict(hq=12, hkv=4, bs=32, budget=140, n_decode=2, decode_ctx=(50, 200),
+                  prompts=((0, 200),)), 256),
+    "one_token_fresh": (dict(hq=4, hkv=4, bs=64, budget=1, n_decode=0, prompts=((0, 1),)), 256),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_bf16_case(name):
+    kw, cus = CASES[name]
+    w = wl.custom(zlib.crc32(name.encode()), **kw)
+    G.say(f"case {name}")
+    r = G.full_pass(w, num_cus=cus)
+    check_append(r, w)
+    G.assert_close(G.out_to_f64(r["out"]), r["ref"], "bf16", name)
+
+
+def test_f32_head_dim_128():
+    w = wl.custom(77, dtype="f32", hq=4, hkv=2, d=128, bs=16, budget=40, n_decode=3,
+                  decode_ctx=(0, 120), prompts=((10, 70),))
+    r = G.full_pass(w)
+    check_append(r, w)
+    G.assert_close(G.out_to_f64(r["out"]), r["ref"], "f32", "f32_d128")
+
+
+def test_deterministic_and_block_permutation_invariant():
+    """Two runs give identical bits, and so does a relabelling of the physical blocks
+    (the reduction order follows logical key order, not physical placement)."""
+    w = wl.custom(5, hq=8, hkv=4, bs=64, budget=300, n_decode=4, decode_ctx=(100, 2000),
+                  prompts=((300, 700),), extra_blocks=7)
+    r = G.full_pass(w, num_cus=100000)
+    gp, hb = r["gp"], r["hb"]
+    q = G.to_dev(r["q"], w.dtype)
+    a = gp.attention_only(hb, q)
+    b = gp.attention_only(hb, q)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), r["out"].view(torch.int16))
+    # relabel: block b -> perm[b]
+    perm = np.random.Generator(np.random.PCG64(3)).permutation(w.num_blocks)
+    pt = torch.from_numpy(perm).cuda()
+    kp, vp = torch.empty_like(gp.cache.k_pool), torch.empty_like(gp.cache.v_pool)
+    kp[pt] = gp.cache.k_pool
+    vp[pt] = gp.cache.v_pool
+    gp2 = G.GpuPass(w, kp, vp, num_cus=100000)
+    hb2 = fg.HostBatch(hb.num_seqs, hb.table_stride)
+    S = hb.num_seqs
+    hb2.query_start[:] = hb.query_start
+    hb2.n_query[:] = hb.n_query
+    hb2.context_len[:] = hb.context_len
+    hb2.block_table[:] = np.where(hb.block_table >= 0, perm[np.maximum(hb.block_table, 0)], -1)
+    hb2.c.num_seqs, hb2.c.num_tokens = S, hb.num_tokens
+    c = gp2.attention_only(hb2, q)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), a.view(torch.int16))
