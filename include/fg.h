@@ -100,10 +100,10 @@ typedef struct fg_ragged_batch {
 } fg_ragged_batch;
 
 typedef struct fg_attention_plan_info {
-  int32_t num_work;          /* work records needed (written if capacity allowed) */
-  int32_t num_groups;        /* key-range split groups */
-  int64_t workspace_bytes;   /* device workspace fg_ragged_attention needs (0: none) */
-  int64_t counter_bytes;     /* leading part of the workspace holding split counters */
+  int32_t num_work;          /* records in the work list: attention records, then one merge
+                                record per split group (written if capacity allowed) */
+  int32_t num_groups;        /* key-range split groups = merge records (the last ones) */
+  int64_t workspace_bytes;   /* device workspace for split partials (0: none needed) */
   int32_t num_q_heads;       /* Hq the plan was made for */
   int32_t num_tokens;        /* T of the batch the plan was made for */
 } fg_attention_plan_info;
@@ -162,12 +162,14 @@ fg_status fg_validate_batch(const fg_cache *cache, const fg_ragged_batch *host);
 fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const void *k_new,
                        const void *v_new, void *stream);
 
-/* Splits the attention of a host batch into work records for one launch (host only).
- * Sequences with few query rows become key-streaming records, chunk rows become 128-row
- * tiles, and long key ranges are split so about num_cus * 4 records exist; records come
- * longest first.  Writes min(num_work, work_capacity) records of FG_WORK_INTS int32 into
- * `work` (host) and fills *info; returns FG_E_ARG when work_capacity < num_work (call
- * with capacity 0 to size).  The caller copies `work` to the device. */
+/* Splits the attention of a host batch into work records (host only).  Sequences with at
+ * most 16 query rows (rows = tokens x query heads per KV head) become key-streaming
+ * records, others become tiles of up to 128 rows; long key ranges are split so that about
+ * num_cus * 4 records' worth of work exists, and records come longest first.  Each split
+ * group also gets a merge record after all attention records.  Writes the num_work records
+ * of FG_WORK_INTS int32 into `work` (host) and fills *info; with work_capacity 0 it only
+ * sizes (FG_OK), with 0 < work_capacity < num_work it returns FG_E_ARG.  The caller copies
+ * `work` to the device. */
 fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *host,
                             int32_t num_q_heads, int32_t num_cus,
                             fg_attention_plan_info *info, int32_t *work,
@@ -176,12 +178,14 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *host,
 /* Exact causal attention of every new token over its sequence's cached history (keys
  * 0 .. context_len[s] + i for new token i, which includes the rows fg_kv_append just
  * wrote): out[t][g] = sum_j softmax_j(scale * q[t][g] . K_j) V_j.  bf16 inputs: products
- * on bf16 MFMA with fp32 accumulation, output rounded to nearest even; fp32 inputs: fp32
- * arithmetic.  `dev` arrays, q, out, work_dev and workspace are device memory; `plan` is
- * the host info fg_attention_plan returned for this batch and work_dev the device copy of
- * its records (both unused for FG_F32).  The first plan->counter_bytes of the workspace
- * must be zero before the first call that uses it (each call leaves them zero again);
- * calls sharing a workspace must be ordered on one stream.
+ * on bf16 MFMA with fp32 accumulation, P rounded to bf16 for the P.V product, output
+ * rounded to nearest even; fp32 inputs: fp32 arithmetic.  `dev` arrays, q, out, work_dev
+ * and workspace are device memory; `plan` is the host info fg_attention_plan returned for
+ * this batch and work_dev the device copy of its records (both unused for FG_F32).  One
+ * launch runs every attention record (decode and chunk rows together); a second, small
+ * launch merges split groups when the plan has any.  The workspace needs no initialisation
+ * (its contents are scratch); calls sharing a workspace must be ordered on one stream.
+ * Results are deterministic (no atomics; merges run in split order).
  * Errors: FG_E_ARG, FG_E_UNSUPPORTED, FG_E_WORKSPACE, FG_E_HIP. */
 fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
                               const fg_attention_plan_info *plan, const int32_t *work_dev,

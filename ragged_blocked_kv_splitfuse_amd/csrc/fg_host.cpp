@@ -291,15 +291,6 @@ fg_status fg_validate_batch(const fg_cache *cache, const fg_ragged_batch *b) {
 // attention work list
 // --------------------------------------------------------------------------------------
 
-namespace {
-struct PlanItem {
-  int32_t s, h, tok0, ntok, klo, khi, mode;
-  int32_t group, split, nsplit;
-  int64_t poff;
-  double cost;
-  int64_t order;
-};
-}  // namespace
 
 fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
                             int32_t num_q_heads, int32_t num_cus, fg_attention_plan_info *info,
@@ -320,11 +311,14 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
   if (cache->cfg.dtype == FG_F32) return FG_OK;  // the fp32 kernel needs no work list
 
   const double e = elem_bytes(cache->cfg.dtype);
+  // Records are planned per "shape" — one (sequence, query-token tile) — because every KV
+  // head of a shape has the same cost and split; heads are expanded when writing out.
   // Cost in "HBM-byte equivalents": a streamed record moves 2*D*e bytes per key; a tile
   // record does 4*D flops per visible (row, key) pair, converted at 8 TB/s against half the
   // bf16 MFMA peak, plus its K/V reads (mostly L2 hits, weighted down).
   const double flop_to_byte = 8.0e12 / (0.5 * 2.5e15);
-  std::vector<PlanItem> base;
+  std::vector<PlanItem> &base = cache->plan_base;
+  base.clear();
   for (int32_t s = 0; s < b->num_seqs; ++s) {
     const int32_t c = b->context_len[s], n = b->n_query[s];
     if (n < 1 || c < 0) return fail(FG_E_DESC, "sequence %d: n_query %d, context_len %d", s, n, c);
@@ -340,18 +334,18 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
         const double pairs = (double)G * ((double)nt * (c + t0) + 0.5 * nt * (nt + 1));
         cost = pairs * 4.0 * D * flop_to_byte + 0.25 * keys * 2.0 * D * e;
       }
-      for (int32_t h = 0; h < Hkv; ++h)
-        base.push_back({s, h, t0, nt, 0, keys, mode, -1, 0, 1, 0, cost, (int64_t)base.size()});
+      base.push_back({s, 0, t0, nt, 0, keys, mode, -1, 0, 1, 0, (float)cost});
     }
   }
   double total = 0;
-  for (auto &it : base) total += it.cost;
+  for (auto &it : base) total += (double)it.cost * Hkv;
   const double target = total / (4.0 * num_cus);
   const int32_t min_tiles = 4;  // a split covers at least 4 key tiles (256 keys)
 
-  std::vector<PlanItem> items;
+  std::vector<PlanItem> &items = cache->plan_items;  // one entry per shape and split
+  items.clear();
   int32_t groups = 0;
-  int64_t poff_bytes = 0;  // partial storage, bytes after the counters
+  int64_t poff_bytes = 0;  // split partial storage in the workspace, bytes
   for (auto &it : base) {
     const int32_t tiles = (it.khi + KEY_TILE - 1) / KEY_TILE;
     int32_t nsplit = 1;
@@ -361,56 +355,72 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
       items.push_back(it);
       continue;
     }
-    const int32_t g = groups++;
-    const int64_t poff = poff_bytes;
-    poff_bytes += (int64_t)nsplit * slot_floats(it.mode, D) * 4;
+    const int32_t g0 = groups;  // heads take groups g0 .. g0 + Hkv - 1
+    groups += Hkv;
+    const int64_t poff = poff_bytes;  // head h's group starts at poff + h * group_bytes
+    const int64_t group_bytes = (int64_t)nsplit * slot_floats(it.mode, D) * 4;
+    poff_bytes += group_bytes * Hkv;
     int32_t tile = 0;
     for (int32_t k = 0; k < nsplit; ++k) {
       const int32_t nt = tiles / nsplit + (k < tiles % nsplit ? 1 : 0);
       PlanItem p = it;
       p.klo = tile * KEY_TILE;
       p.khi = std::min(it.khi, (tile + nt) * KEY_TILE);
-      p.group = g;
+      p.group = g0;
       p.split = k;
       p.nsplit = nsplit;
       p.poff = poff;
-      p.cost = it.cost * nt / tiles;
+      p.cost = it.cost * (float)nt / (float)tiles;
       tile += nt;
       items.push_back(p);
     }
   }
-  // longest first (stable), so the long-running records start early
-  std::stable_sort(items.begin(), items.end(),
-                   [](const PlanItem &a, const PlanItem &b2) { return a.cost > b2.cost; });
+  // longest first (ties keep their order), so the long-running records start early
+  std::vector<std::pair<float, int32_t>> &order = cache->plan_order;
+  order.resize(items.size());
+  for (size_t i = 0; i < items.size(); ++i) order[i] = {-items[i].cost, (int32_t)i};
+  std::sort(order.begin(), order.end());
 
-  const int64_t counter_bytes = ((int64_t)groups * 4 + 255) / 256 * 256;
-  const int64_t ws = groups ? counter_bytes + poff_bytes : 0;
+  const int64_t ws = groups ? poff_bytes : 0;
   if ((ws / 4) > INT32_MAX) return fail(FG_E_UNSUPPORTED, "workspace beyond 8 GiB");
-  if ((int64_t)items.size() > INT32_MAX) return fail(FG_E_UNSUPPORTED, "too many work records");
-  info->num_work = (int32_t)items.size();
+  const int64_t n_main = (int64_t)items.size() * Hkv;
+  if (n_main + groups > INT32_MAX) return fail(FG_E_UNSUPPORTED, "too many records");
+  info->num_work = (int32_t)(n_main + groups);
   info->num_groups = groups;
-  info->counter_bytes = groups ? counter_bytes : 0;
   info->workspace_bytes = ws;
   if (work_capacity < info->num_work) {
     if (work_capacity == 0) return FG_OK;  // sizing call
     return fail(FG_E_ARG, "work capacity %d < %d records", work_capacity, info->num_work);
   }
   if (info->num_work > 0 && !work) return fail(FG_E_ARG, "work is null");
+  int32_t *w = work;
+  int32_t *merge = work + n_main * FG_WORK_INTS;  // merge record of group g at merge[g]
   for (size_t i = 0; i < items.size(); ++i) {
-    const PlanItem &p = items[i];
-    int32_t *w = work + i * FG_WORK_INTS;
-    w[W_SEQ] = p.s;
-    w[W_KVH] = p.h;
-    w[W_TOK0] = p.tok0;
-    w[W_NTOK] = p.ntok;
-    w[W_KLO] = p.klo;
-    w[W_KHI] = p.khi;
-    w[W_MODE] = p.mode;
-    w[W_GROUP] = p.group;
-    w[W_SPLIT] = p.split;
-    w[W_NSPLIT] = p.nsplit;
-    w[W_POFF] = p.group >= 0 ? (int32_t)((counter_bytes + p.poff) / 4) : 0;
-    w[W_RES] = 0;
+    const PlanItem &p = items[order[i].second];
+    const int64_t group_bytes = (int64_t)p.nsplit * slot_floats(p.mode, D) * 4;
+    for (int32_t h = 0; h < Hkv; ++h, w += FG_WORK_INTS) {
+      const int32_t g = p.group >= 0 ? p.group + h : -1;
+      const int32_t poff = p.group >= 0 ? (int32_t)((p.poff + h * group_bytes) / 4) : 0;
+      w[W_SEQ] = p.s;
+      w[W_KVH] = h;
+      w[W_TOK0] = p.tok0;
+      w[W_NTOK] = p.ntok;
+      w[W_KLO] = p.klo;
+      w[W_KHI] = p.khi;
+      w[W_MODE] = p.mode;
+      w[W_GROUP] = g;
+      w[W_SPLIT] = p.split;
+      w[W_NSPLIT] = p.nsplit;
+      w[W_POFF] = poff;
+      w[W_RES] = 0;
+      if (g >= 0 && p.split == 0) {
+        int32_t *m = merge + (size_t)g * FG_WORK_INTS;
+        std::memcpy(m, w, FG_WORK_INTS * sizeof(int32_t));
+        m[W_KLO] = 0;
+        m[W_KHI] = 0;
+        m[W_SPLIT] = -1;  // marks a merge record
+      }
+    }
   }
   return FG_OK;
 }

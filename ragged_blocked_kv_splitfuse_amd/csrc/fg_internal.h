@@ -6,6 +6,15 @@
 
 #include "fg.h"
 
+namespace fgi {
+// One attention work record while planning (before it is written out).
+struct PlanItem {
+  int32_t s, h, tok0, ntok, klo, khi, mode, group, split, nsplit;
+  int64_t poff;
+  float cost;
+};
+}  // namespace fgi
+
 struct fg_cache {
   fg_cache_config cfg;
   void *k_pool;
@@ -13,6 +22,9 @@ struct fg_cache {
   int32_t bs_log2;
   std::vector<int32_t> free_stack;  // top = back(); handed out from the top
   std::vector<uint8_t> is_free;     // per physical id
+  // planner scratch, reused across calls so planning allocates nothing in steady state
+  mutable std::vector<fgi::PlanItem> plan_base, plan_items;
+  mutable std::vector<std::pair<float, int32_t>> plan_order;
 };
 
 namespace fgi {

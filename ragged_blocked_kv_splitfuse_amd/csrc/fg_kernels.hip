@@ -28,6 +28,7 @@
 using namespace fgi;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
@@ -50,21 +51,12 @@ __device__ __forceinline__ uint4 ld16(const void *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet).
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  uint32_t u = __builtin_bit_cast(uint32_t, x);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ __forceinline__ bf16x8 pack_bf16x8(const float *p) {
-  uint4 r;
-  r.x = bf16_bits(p[0]) | (bf16_bits(p[1]) << 16);
-  r.y = bf16_bits(p[2]) | (bf16_bits(p[3]) << 16);
-  r.z = bf16_bits(p[4]) | (bf16_bits(p[5]) << 16);
-  r.w = bf16_bits(p[6]) | (bf16_bits(p[7]) << 16);
-  return as_bf16x8(r);
+// eight fp32 values -> eight bf16 (hardware round-to-nearest-even conversion)
+__device__ __forceinline__ bf16x8 to_bf16x8(const float *p) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)p[i];
+  return r;
 }
 
 // keep elements i < n of eight packed bf16 values, zero the rest (n in [0, 8])
@@ -79,9 +71,7 @@ __device__ __forceinline__ uint4 keep_first(uint4 v, int n) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__device__ __forceinline__ float wave_max_xor(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
-}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ int clamp_block(int b, int nb) { return b < 0 ? 0 : (b >= nb ? nb - 1 : b); }
 
@@ -102,8 +92,7 @@ struct Params {
   const u16 *k_pool;
   const u16 *v_pool;
   u16 *out;
-  float *ws;          // workspace as floats (partials)
-  int32_t *counters;  // workspace head (split counters)
+  float *ws;          // workspace as floats (split partials)
   int64_t ws_floats;
   int32_t Hq, Hkv, G, bs, bs_log2, num_blocks;
   float sl2;          // scale * log2(e)
@@ -129,63 +118,107 @@ __device__ __forceinline__ Rec load_rec(const int32_t *w) {
   return r;
 }
 
+__device__ __forceinline__ bool rec_fits_workspace(const Params &P, const Rec &R) {
+  return R.group < 0 ||
+         (int64_t)R.poff + (int64_t)R.nsplit * slot_floats(R.mode, D) <= P.ws_floats;
+}
+
 // Final normalisation and bf16 store of 8 consecutive features of one query row.
 __device__ __forceinline__ void store_out8(const Params &P, int t, int head, int d0,
                                            const float *o, float inv_l) {
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = o[i] * inv_l;
-  bf16x8 b = pack_bf16x8(v);
-  *reinterpret_cast<uint4 *>(P.out + ((size_t)t * P.Hq + head) * D + d0) =
-      __builtin_bit_cast(uint4, b);
+  *reinterpret_cast<bf16x8 *>(P.out + ((size_t)t * P.Hq + head) * D + d0) = to_bf16x8(v);
 }
 
-// The last workgroup of a split group merges every split's (m, l, acc) partial in split
-// order (so the result does not depend on which workgroup finished last) and writes O.
-__device__ void merge_splits(const Params &P, const Rec &R, int rows, int c0_tok, int qs) {
+// Online softmax over one 64-key tile for one 16-row MFMA tile (FlashAttention's running
+// max / running sum).  s[kh][a][j] holds the raw score of key key0 + 32kh + 4a + j for this
+// lane's row (key0 = k0 + 8g).  The running max m lives in the scaled log2 domain; p =
+// 2^(s*scale*log2e - m).  Updates m, l (this lane's partial row sum), rescales acc when a
+// row's max moved, and returns P packed to bf16 as the B operands of the P.V product.
+__device__ __forceinline__ void online_softmax(f32x4 (&s)[2][2], bool need_mask, int key0,
+                                               int lim, int khi, float sl2, float &m, float &l,
+                                               f32x4 *acc, bf16x8 (&pf)[2]) {
+  if (need_mask) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = key0 + 32 * kh + 4 * a + j;
+          if (key > lim || key >= khi) s[kh][a][j] = NEG_INF;
+        }
+  }
+  float mx = NEG_INF;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[kh][a][j]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(m, mx * sl2);
+  const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+  const float alpha = fast_exp2(m - m_use);
+  float psum = 0.f;
+  float p[2][8];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e = fast_exp2(fmaf(s[kh][a][j], sl2, -m_use));
+        p[kh][4 * a + j] = e;
+        psum += e;
+      }
+  l = l * alpha + psum;
+  m = m_new;
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
+  }
+  pf[0] = to_bf16x8(p[0]);
+  pf[1] = to_bf16x8(p[1]);
+}
+
+// Combine: the merge record of a split group reads every split's (m, l, acc) partial in
+// split order (deterministic) and writes O.  Runs in its own launch after the main kernel.
+__device__ void merge_splits(const Params &P, const Rec &R) {
   const int64_t slot = slot_floats(R.mode, D);
   const int cap = R.mode == MODE_STREAM ? STREAM_ROWS : TILE_ROWS;
+  const int rows = R.ntok * P.G;
+  const int qs = P.query_start[R.s];
   for (int idx = threadIdx.x; idx < rows * (D / 8); idx += NT) {
     const int row = idx / (D / 8), chunk = idx % (D / 8);
     float M = NEG_INF;
-    for (int k = 0; k < R.nsplit; ++k) {
-      const float *sp = P.ws + R.poff + k * slot;
-      M = fmaxf(M, sp[cap * D + row]);
-    }
+    for (int k = 0; k < R.nsplit; ++k) M = fmaxf(M, P.ws[R.poff + k * slot + cap * D + row]);
     float L = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int k = 0; k < R.nsplit; ++k) {
       const float *sp = P.ws + R.poff + k * slot;
       const float m = sp[cap * D + row];
-      const float f = (m == NEG_INF) ? 0.f : exp2f(m - M);
+      const float f = (m == NEG_INF) ? 0.f : fast_exp2(m - M);
       L += sp[cap * D + cap + row] * f;
       const float4 a = *reinterpret_cast<const float4 *>(sp + row * D + chunk * 8);
       const float4 b = *reinterpret_cast<const float4 *>(sp + row * D + chunk * 8 + 4);
       o[0] += a.x * f; o[1] += a.y * f; o[2] += a.z * f; o[3] += a.w * f;
       o[4] += b.x * f; o[5] += b.y * f; o[6] += b.z * f; o[7] += b.w * f;
     }
-    const int t = qs + c0_tok + row / P.G;
+    const int t = qs + R.tok0 + row / P.G;
     const int head = R.h * P.G + row % P.G;
     if (t < P.num_tokens) store_out8(P, t, head, chunk * 8, o, 1.f / L);
   }
 }
 
-// Returns true in every thread of the workgroup that must merge the group (the last one).
-__device__ bool arrive_last(const Params &P, const Rec &R, int *flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(P.counters + R.group, 1);
-    *flag = (prev == R.nsplit - 1);
-  }
-  __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-__device__ __forceinline__ void reset_counter(const Params &P, const Rec &R) {
-  __syncthreads();
-  if (threadIdx.x == 0) atomicExch(P.counters + R.group, 0);
+// Address of key `key` of KV head h (K pool) and of the 8-key run starting at `key` for
+// feature 0 (V pool).  BIG: blocks hold >= 64 keys, so a 64-key tile lies in one block and
+// keys past the sequence end still sit inside an allocated block.
+template <bool BIG>
+__device__ __forceinline__ int tile_block(const Params &P, const int32_t *bt, int k0) {
+  return BIG ? clamp_block(bt[k0 >> P.bs_log2], P.num_blocks) : 0;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -193,6 +226,7 @@ __device__ __forceinline__ void reset_counter(const Params &P, const Rec &R) {
 // from HBM into MFMA operand registers (no LDS staging, no barriers), then the four waves
 // merge their running states through LDS.
 // ---------------------------------------------------------------------------------------
+template <bool BIG>
 __device__ void stream_record(const Params &P, const Rec &R, unsigned char *smem) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
   const int c = P.context_len[R.s], qs = P.query_start[R.s];
@@ -200,49 +234,56 @@ __device__ void stream_record(const Params &P, const Rec &R, unsigned char *smem
   const int rows = R.ntok * P.G;
   const int32_t *bt = P.block_table + (size_t)R.s * P.table_stride;
   const int bs_mask = P.bs - 1;
+  const size_t head_stride = (size_t)P.bs * D;  // elements per (block, head) in either pool
 
-  // this lane's query row (r) and its causal limit
   const bool row_ok = r < rows;
   const int row_tok = R.tok0 + r / P.G;
-  const int lim = c + row_tok;  // keys 0 .. lim are visible
+  const int lim = c + row_tok;  // keys 0 .. lim are visible to this lane's row
   bf16x8 qf[D / 32];
   {
     const int t = qs + row_tok, head = R.h * P.G + r % P.G;
     const u16 *qp = P.q + ((size_t)t * P.Hq + head) * D + 8 * g;
 #pragma unroll
     for (int dc = 0; dc < D / 32; ++dc)
-      qf[dc] = (row_ok && t < P.num_tokens) ? as_bf16x8(ld16(qp + 32 * dc)) : as_bf16x8(make_uint4(0, 0, 0, 0));
+      qf[dc] = (row_ok && t < P.num_tokens) ? as_bf16x8(ld16(qp + 32 * dc))
+                                           : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
-
   float m_run = NEG_INF, l_run = 0.f;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int t_begin = R.klo / KT, t_end = (R.khi + KT - 1) / KT;
-  const size_t head_stride = (size_t)P.bs * D;  // elements per (block, head) in either pool
   for (int kt = t_begin + w; kt < t_end; kt += NW) {
     const int k0 = kt * KT;
-    // ---- K operand: 2 halves x 2 sub-tiles x D/32 chunks, key rows permuted -------------
+    const int blk_t = tile_block<BIG>(P, bt, k0);
+    // ---- K operand: key rows permuted so the S^T layout feeds P.V directly ------------
     bf16x8 kf[2][2][D / 32];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
-        const int key = min(k0 + 32 * kh + 8 * (r >> 2) + 4 * a + (r & 3), L - 1);
-        const int blk = clamp_block(bt[key >> P.bs_log2], P.num_blocks);
+        int key = k0 + 32 * kh + 8 * (r >> 2) + 4 * a + (r & 3);
+        int blk = blk_t;
+        if (!BIG) {
+          key = min(key, L - 1);
+          blk = clamp_block(bt[key >> P.bs_log2], P.num_blocks);
+        }
         const u16 *kp = P.k_pool + ((size_t)blk * P.Hkv + R.h) * head_stride +
                         (size_t)(key & bs_mask) * D + 8 * g;
 #pragma unroll
         for (int dc = 0; dc < D / 32; ++dc) kf[kh][a][dc] = as_bf16x8(ld16(kp + 32 * dc));
       }
-    // ---- V^T operand: 2 halves x D/16 feature tiles, 8 consecutive keys per lane --------
+    // ---- V^T operand: 8 consecutive keys of one feature per lane ------------------------
     uint4 vr[2][D / 16];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       const int key0 = k0 + 32 * kh + 8 * g;
-      const int keyc = min(key0, (L - 1) & ~7);
-      const int blk = clamp_block(bt[keyc >> P.bs_log2], P.num_blocks);
+      int keyc = key0, blk = blk_t;
+      if (!BIG) {
+        keyc = min(key0, (L - 1) & ~7);
+        blk = clamp_block(bt[keyc >> P.bs_log2], P.num_blocks);
+      }
       const u16 *vp = P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (keyc & bs_mask) +
                       (size_t)r * P.bs;
 #pragma unroll
@@ -253,7 +294,7 @@ __device__ void stream_record(const Params &P, const Rec &R, unsigned char *smem
         for (int dt = 0; dt < D / 16; ++dt) vr[kh][dt] = keep_first(vr[kh][dt], nvalid);
       }
     }
-    // ---- S^T = K . Q^T ---------------------------------------------------------------
+    // ---- S^T = K . Q^T, online softmax, O^T += V^T . P^T ------------------------------
     f32x4 st[2][2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -263,48 +304,15 @@ __device__ void stream_record(const Params &P, const Rec &R, unsigned char *smem
 #pragma unroll
         for (int dc = 0; dc < D / 32; ++dc) st[kh][a] = mfma_bf16(kf[kh][a][dc], qf[dc], st[kh][a]);
       }
-    // ---- online softmax (lane holds keys k0 + 32kh + 8g + 4a + j of row r) ---------------
     const bool need_mask = (k0 + KT > R.khi) || (k0 + KT - 1 > c + R.tok0);
-    float sv[2][8];
-    float tmax = NEG_INF;
+    bf16x8 pf[2];
+    online_softmax(st, need_mask, k0 + 8 * g, lim, R.khi, P.sl2, m_run, l_run, acc, pf);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = k0 + 32 * kh + 8 * g + 4 * a + j;
-          float x = st[kh][a][j] * P.sl2;
-          if (need_mask && (key > lim || key >= R.khi)) x = NEG_INF;
-          sv[kh][4 * a + j] = x;
-          tmax = fmaxf(tmax, x);
-        }
-    tmax = wave_max_xor(tmax, 16);
-    tmax = wave_max_xor(tmax, 32);
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float psum = 0.f;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sv[kh][i] = exp2f(sv[kh][i] - m_use);
-        psum += sv[kh][i];
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
-    // ---- O^T += V^T . P^T ------------------------------------------------------------
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const bf16x8 pf = pack_bf16x8(sv[kh]);
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma_bf16(as_bf16x8(vr[kh][dt]), pf, acc[dt]);
-    }
+      for (int dt = 0; dt < D / 16; ++dt)
+        acc[dt] = mfma_bf16(as_bf16x8(vr[kh][dt]), pf[kh], acc[dt]);
   }
-  // row sum over the four lanes that share row r
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
 
@@ -321,41 +329,31 @@ __device__ void stream_record(const Params &P, const Rec &R, unsigned char *smem
     sl[w * STREAM_ROWS + r] = l_run;
   }
   __syncthreads();
-  {
-    const int row = threadIdx.x >> 4, chunk = threadIdx.x & 15;  // 16 rows x 16 chunks of 8
-    float M = NEG_INF;
+  const int row = threadIdx.x >> 4, chunk = threadIdx.x & 15;  // 16 rows x 16 chunks of 8
+  if (row >= rows) return;
+  float M = NEG_INF;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm[ww * STREAM_ROWS + row]);
-    float Lsum = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm[ww * STREAM_ROWS + row]);
+  float Lsum = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float m = sm[ww * STREAM_ROWS + row];
-      const float f = (m == NEG_INF) ? 0.f : exp2f(m - M);
-      Lsum += sl[ww * STREAM_ROWS + row] * f;
-      const float *src = so + (ww * STREAM_ROWS + row) * OP + chunk * 8;
+  for (int ww = 0; ww < NW; ++ww) {
+    const float m = sm[ww * STREAM_ROWS + row];
+    const float f = (m == NEG_INF) ? 0.f : fast_exp2(m - M);
+    Lsum += sl[ww * STREAM_ROWS + row] * f;
+    const float *src = so + (ww * STREAM_ROWS + row) * OP + chunk * 8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] += src[i] * f;
-    }
-    if (row < rows) {
-      if (R.group < 0) {
-        const int t = qs + R.tok0 + row / P.G;
-        if (t < P.num_tokens) store_out8(P, t, R.h * P.G + row % P.G, chunk * 8, o, 1.f / Lsum);
-      } else {
-        float *sp = P.ws + R.poff + (int64_t)R.split * slot_floats(MODE_STREAM, D);
-        *reinterpret_cast<float4 *>(sp + row * D + chunk * 8) = make_float4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<float4 *>(sp + row * D + chunk * 8 + 4) = make_float4(o[4], o[5], o[6], o[7]);
-        if (chunk == 0) {
-          sp[STREAM_ROWS * D + row] = M;
-          sp[STREAM_ROWS * D + STREAM_ROWS + row] = Lsum;
-        }
-      }
-    }
+    for (int i = 0; i < 8; ++i) o[i] += src[i] * f;
   }
-  if (R.group >= 0) {
-    int *flag = reinterpret_cast<int *>(sl + NW * STREAM_ROWS);
-    if (arrive_last(P, R, flag)) {
-      merge_splits(P, R, rows, R.tok0, qs);
-      reset_counter(P, R);
+  if (R.group < 0) {
+    const int t = qs + R.tok0 + row / P.G;
+    if (t < P.num_tokens) store_out8(P, t, R.h * P.G + row % P.G, chunk * 8, o, 1.f / Lsum);
+  } else {
+    float *sp = P.ws + R.poff + (int64_t)R.split * slot_floats(MODE_STREAM, D);
+    *reinterpret_cast<float4 *>(sp + row * D + chunk * 8) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4 *>(sp + row * D + chunk * 8 + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    if (chunk == 0) {
+      sp[STREAM_ROWS * D + row] = M;
+      sp[STREAM_ROWS * D + STREAM_ROWS + row] = Lsum;
     }
   }
 }
@@ -369,6 +367,7 @@ constexpr int KTILE_ELEMS = KT * D;   // K tile [64 keys][128]
 constexpr int VTILE_ELEMS = D * KT;   // V^T tile [128 features][64 keys]
 constexpr int BUF_ELEMS = KTILE_ELEMS + VTILE_ELEMS;
 
+template <bool BIG>
 __device__ void tile_record(const Params &P, const Rec &R, unsigned char *smem) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r = lane & 15;
   const int c = P.context_len[R.s], qs = P.query_start[R.s];
@@ -406,23 +405,35 @@ __device__ void tile_record(const Params &P, const Rec &R, unsigned char *smem) 
   uint4 kreg[4], vreg[4];
   auto gload = [&](int kt) {
     const int k0 = kt * KT;
+    const int blk_t = tile_block<BIG>(P, bt, k0);
+    const u16 *kb = P.k_pool + ((size_t)blk_t * P.Hkv + R.h) * head_stride + (size_t)(k0 & bs_mask) * D;
+    const u16 *vb = P.v_pool + ((size_t)blk_t * P.Hkv + R.h) * head_stride + (k0 & bs_mask);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int qi = tid + NT * p;
-      const int key = min(k0 + (qi >> 4), L - 1);
-      const int blk = clamp_block(bt[key >> P.bs_log2], P.num_blocks);
-      kreg[p] = ld16(P.k_pool + ((size_t)blk * P.Hkv + R.h) * head_stride +
-                     (size_t)(key & bs_mask) * D + 8 * (qi & 15));
+      if (BIG) {
+        kreg[p] = ld16(kb + (size_t)(qi >> 4) * D + 8 * (qi & 15));
+      } else {
+        const int key = min(k0 + (qi >> 4), L - 1);
+        const int blk = clamp_block(bt[key >> P.bs_log2], P.num_blocks);
+        kreg[p] = ld16(P.k_pool + ((size_t)blk * P.Hkv + R.h) * head_stride +
+                       (size_t)(key & bs_mask) * D + 8 * (qi & 15));
+      }
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int qi = tid + NT * p;
       const int d = qi >> 3;
       const int key0 = k0 + 8 * (qi & 7);
-      const int keyc = min(key0, (L - 1) & ~7);
-      const int blk = clamp_block(bt[keyc >> P.bs_log2], P.num_blocks);
-      uint4 v = ld16(P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)d * P.bs +
-                     (keyc & bs_mask));
+      uint4 v;
+      if (BIG) {
+        v = ld16(vb + (size_t)d * P.bs + 8 * (qi & 7));
+      } else {
+        const int keyc = min(key0, (L - 1) & ~7);
+        const int blk = clamp_block(bt[keyc >> P.bs_log2], P.num_blocks);
+        v = ld16(P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)d * P.bs +
+                 (keyc & bs_mask));
+      }
       if (key0 + 8 > R.khi) v = keep_first(v, min(max(R.khi - key0, 0), 8));
       vreg[p] = v;
     }
@@ -479,43 +490,11 @@ __device__ void tile_record(const Params &P, const Rec &R, unsigned char *smem) 
         }
       const bool need_mask = (k0 + KT > R.khi) || (k0 + KT - 1 > c + R.tok0);
       bf16x8 pf[2][2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        if (rt >= nrt) break;
-        float sv[2][8];
-        float tmax = NEG_INF;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int key = k0 + 32 * kh + 8 * g + 4 * a + j;
-              float x = st[rt][kh][a][j] * P.sl2;
-              if (need_mask && (key > lim[rt] || key >= R.khi)) x = NEG_INF;
-              sv[kh][4 * a + j] = x;
-              tmax = fmaxf(tmax, x);
-            }
-        tmax = wave_max_xor(tmax, 16);
-        tmax = wave_max_xor(tmax, 32);
-        const float m_new = fmaxf(m_run[rt], tmax);
-        const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-        const float alpha = exp2f(m_run[rt] - m_use);
-        float psum = 0.f;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            sv[kh][i] = exp2f(sv[kh][i] - m_use);
-            psum += sv[kh][i];
-          }
-        l_run[rt] = l_run[rt] * alpha + psum;
-        m_run[rt] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) acc[rt][dt] *= alpha;
-        pf[rt][0] = pack_bf16x8(sv[0]);
-        pf[rt][1] = pack_bf16x8(sv[1]);
-      }
+      online_softmax(st[0], need_mask, k0 + 8 * g, lim[0], R.khi, P.sl2, m_run[0], l_run[0],
+                     acc[0], pf[0]);
+      if (nrt > 1)
+        online_softmax(st[1], need_mask, k0 + 8 * g, lim[1], R.khi, P.sl2, m_run[1], l_run[1],
+                       acc[1], pf[1]);
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -531,7 +510,7 @@ __device__ void tile_record(const Params &P, const Rec &R, unsigned char *smem) 
     __syncthreads();
   }
 
-  // ---- epilogue ------------------------------------------------------------------------
+  // ---- epilogue: normalise and store, or write the split partial ------------------------
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     if (rt >= nrt) break;
@@ -548,11 +527,13 @@ __device__ void tile_record(const Params &P, const Rec &R, unsigned char *smem) 
       u16 *op = P.out + ((size_t)t * P.Hq + head) * D + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        const f32x4 a = acc[rt][dt];
-        uint2 v;
-        v.x = bf16_bits(a[0] * inv) | (bf16_bits(a[1] * inv) << 16);
-        v.y = bf16_bits(a[2] * inv) | (bf16_bits(a[3] * inv) << 16);
-        *reinterpret_cast<uint2 *>(op + 16 * dt) = v;
+        const f32x4 a = acc[rt][dt] * inv;
+        bf16x4 v;
+        v[0] = (__bf16)a[0];
+        v[1] = (__bf16)a[1];
+        v[2] = (__bf16)a[2];
+        v[3] = (__bf16)a[3];
+        *reinterpret_cast<bf16x4 *>(op + 16 * dt) = v;
       }
     } else {
       float *sp = P.ws + R.poff + (int64_t)R.split * slot_floats(MODE_TILE, D);
@@ -565,29 +546,28 @@ __device__ void tile_record(const Params &P, const Rec &R, unsigned char *smem) 
       }
     }
   }
-  if (R.group >= 0) {
-    int *flag = reinterpret_cast<int *>(smem);  // tile buffers are no longer needed
-    __syncthreads();
-    if (arrive_last(P, R, flag)) {
-      merge_splits(P, R, rows, R.tok0, qs);
-      reset_counter(P, R);
-    }
-  }
 }
 
 constexpr int SMEM_BYTES = 2 * BUF_ELEMS * 2;  // 64 KiB: two K + V^T tile buffers
 
+// One launch serves every record of the pass: stream records (decode rows, HBM-bound) and
+// tile records (chunk rows, MFMA-bound); the branch is uniform per workgroup.
+template <bool BIG>
 __global__ __launch_bounds__(NT, 2) void attention_bf16_kernel(Params P) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
   const Rec R = load_rec(P.work + (size_t)blockIdx.x * FG_WORK_INTS);
-  if (R.s < 0 || R.mode < 0) return;
-  if (R.group >= 0 &&
-      (int64_t)R.poff + (int64_t)R.nsplit * slot_floats(R.mode, D) > P.ws_floats)
-    return;  // record inconsistent with the workspace: never write outside it
+  if (R.s < 0 || !rec_fits_workspace(P, R)) return;  // never write outside the workspace
   if (R.mode == MODE_STREAM)
-    stream_record(P, R, smem);
+    stream_record<BIG>(P, R, smem);
   else
-    tile_record(P, R, smem);
+    tile_record<BIG>(P, R, smem);
+}
+
+// Merge records follow the attention records in the work list, one per split group.
+__global__ __launch_bounds__(NT) void attention_combine_kernel(Params P, int32_t first) {
+  const Rec R = load_rec(P.work + ((size_t)first + blockIdx.x) * FG_WORK_INTS);
+  if (R.s < 0 || R.group < 0 || !rec_fits_workspace(P, R)) return;
+  merge_splits(P, R);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -656,41 +636,72 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// KV append: one workgroup per new token.  K rows are copied whole (16-byte chunks); V rows
-// are scattered feature by feature into the feature-major V block.
+// KV append: one workgroup per (tile of 64 consecutive new tokens, KV head).  K rows are
+// copied whole in 16-byte chunks (a K block row is contiguous).  V rows are staged in LDS
+// and written feature by feature with lanes on consecutive tokens, so the tokens of a prompt
+// chunk that share a block fill consecutive slots of each feature row (coalesced stores).
 // ---------------------------------------------------------------------------------------
-template <typename T>
+constexpr int APPEND_TOKENS = 64;
+
+template <typename T, int HD>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const int32_t *__restrict__ query_start, const int32_t *__restrict__ context_len,
     const int32_t *__restrict__ block_table, int32_t table_stride, int32_t num_seqs,
-    const T *__restrict__ k_new, const T *__restrict__ v_new, T *__restrict__ k_pool,
-    T *__restrict__ v_pool, int32_t Hkv, int32_t hd, int32_t bs, int32_t bs_log2,
+    int32_t num_tokens, const T *__restrict__ k_new, const T *__restrict__ v_new,
+    T *__restrict__ k_pool, T *__restrict__ v_pool, int32_t Hkv, int32_t bs, int32_t bs_log2,
     int32_t num_blocks) {
-  const int t = blockIdx.x;
-  int lo = 0, hi = num_seqs;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (query_start[mid] <= t) lo = mid; else hi = mid;
+  constexpr int VEC = 16 / sizeof(T);            // elements per 16-byte chunk
+  constexpr int CPR = HD / VEC;                  // chunks per row
+  constexpr int ROWP = HD + 4 / sizeof(T);       // LDS row padded by one dword
+  __shared__ int dblk[APPEND_TOKENS], dslot[APPEND_TOKENS];
+  __shared__ T vt[APPEND_TOKENS * ROWP];
+  const int t0 = blockIdx.x * APPEND_TOKENS, h = blockIdx.y, tid = threadIdx.x;
+  if (tid < APPEND_TOKENS) {
+    const int t = t0 + tid;
+    int blk = -1, slot = 0;
+    if (t < num_tokens) {
+      int lo = 0, hi = num_seqs;  // s with query_start[s] <= t < query_start[s+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (query_start[mid] <= t) lo = mid; else hi = mid;
+      }
+      const int pos = context_len[lo] + (t - query_start[lo]);
+      const int b = block_table[(size_t)lo * table_stride + (pos >> bs_log2)];
+      if (b >= 0 && b < num_blocks) {  // validated on the host; never write out of range
+        blk = b;
+        slot = pos & (bs - 1);
+      }
+    }
+    dblk[tid] = blk;
+    dslot[tid] = slot;
   }
-  const int s = lo;
-  const int pos = context_len[s] + (t - query_start[s]);
-  const int blk = block_table[(size_t)s * table_stride + (pos >> bs_log2)];
-  if (blk < 0 || blk >= num_blocks) return;  // validated on the host; never write out of range
-  const int slot = pos & (bs - 1);
-  const int row = Hkv * hd;
-  // K: Hkv rows of hd elements, each contiguous at (blk, h, slot)
-  constexpr int V16 = 16 / sizeof(T);
-  const int chunks_per_head = hd / V16;
-  for (int i = threadIdx.x; i < Hkv * chunks_per_head; i += blockDim.x) {
-    const int h = i / chunks_per_head, ch = i % chunks_per_head;
-    const uint4 v = *reinterpret_cast<const uint4 *>(k_new + (size_t)t * row + h * hd + ch * V16);
-    *reinterpret_cast<uint4 *>(k_pool + (((size_t)blk * Hkv + h) * bs + slot) * hd + ch * V16) = v;
+  __syncthreads();
+  const size_t row_in = (size_t)Hkv * HD;  // elements per token in k_new / v_new
+  for (int q = tid; q < APPEND_TOKENS * CPR; q += blockDim.x) {
+    const int tok = q / CPR, c = q % CPR;
+    const int blk = dblk[tok];
+    if (blk < 0) continue;
+    const uint4 v = *reinterpret_cast<const uint4 *>(k_new + (t0 + tok) * row_in + h * HD + c * VEC);
+    *reinterpret_cast<uint4 *>(k_pool + (((size_t)blk * Hkv + h) * bs + dslot[tok]) * HD +
+                               c * VEC) = v;
   }
-  // V: element (h, d) goes to ((blk*Hkv + h)*hd + d)*bs + slot
-  for (int i = threadIdx.x; i < row; i += blockDim.x) {
-    const int h = i / hd, d = i % hd;
-    v_pool[(((size_t)blk * Hkv + h) * hd + d) * bs + slot] = v_new[(size_t)t * row + i];
+  for (int q = tid; q < APPEND_TOKENS * CPR; q += blockDim.x) {
+    const int tok = q / CPR, c = q % CPR;
+    if (t0 + tok >= num_tokens) continue;
+    const uint4 v = *reinterpret_cast<const uint4 *>(v_new + (t0 + tok) * row_in + h * HD + c * VEC);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(vt + tok * ROWP + c * VEC);
+    dst[0] = v.x;
+    dst[1] = v.y;
+    dst[2] = v.z;
+    dst[3] = v.w;
   }
+  __syncthreads();
+  const int tok = tid % APPEND_TOKENS;
+  const int blk = dblk[tok];
+  if (blk < 0) return;
+  T *vrow = v_pool + ((size_t)blk * Hkv + h) * HD * bs + dslot[tok];
+  for (int d = tid / APPEND_TOKENS; d < HD; d += blockDim.x / APPEND_TOKENS)
+    vrow[(size_t)d * bs] = vt[tok * ROWP + d];
 }
 
 }  // namespace
@@ -712,20 +723,21 @@ fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const 
     return fail(FG_E_ARG, "k_new, v_new and both pools must be device pointers");
   const fg_cache_config &c = cache->cfg;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid(dev->num_tokens), block(256);
-  if (c.dtype == FG_BF16) {
-    hipLaunchKernelGGL(kv_append_kernel<u16>, grid, block, 0, st, dev->query_start,
-                       dev->context_len, dev->block_table, dev->table_stride, dev->num_seqs,
-                       (const u16 *)k_new, (const u16 *)v_new, (u16 *)cache->k_pool,
-                       (u16 *)cache->v_pool, c.num_kv_heads, c.head_dim, c.block_size,
-                       cache->bs_log2, c.num_blocks);
-  } else {
-    hipLaunchKernelGGL(kv_append_kernel<float>, grid, block, 0, st, dev->query_start,
-                       dev->context_len, dev->block_table, dev->table_stride, dev->num_seqs,
-                       (const float *)k_new, (const float *)v_new, (float *)cache->k_pool,
-                       (float *)cache->v_pool, c.num_kv_heads, c.head_dim, c.block_size,
-                       cache->bs_log2, c.num_blocks);
-  }
+  const dim3 grid((dev->num_tokens + APPEND_TOKENS - 1) / APPEND_TOKENS, c.num_kv_heads);
+  const dim3 block(256);
+#define FG_APPEND(T, HD)                                                                      \
+  hipLaunchKernelGGL((kv_append_kernel<T, HD>), grid, block, 0, st, dev->query_start,           \
+                     dev->context_len, dev->block_table, dev->table_stride, dev->num_seqs,     \
+                     dev->num_tokens, (const T *)k_new, (const T *)v_new, (T *)cache->k_pool,  \
+                     (T *)cache->v_pool, c.num_kv_heads, c.block_size, cache->bs_log2,         \
+                     c.num_blocks)
+  if (c.dtype == FG_BF16)
+    FG_APPEND(u16, 128);
+  else if (c.head_dim == 64)
+    FG_APPEND(float, 64);
+  else
+    FG_APPEND(float, 128);
+#undef FG_APPEND
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_E_HIP, "kv_append launch: %s", hipGetErrorString(e));
   return FG_OK;
@@ -768,7 +780,9 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
     if (plan->num_q_heads != num_q_heads || plan->num_tokens != dev->num_tokens)
       return fail(FG_E_ARG, "plan was made for another batch (Hq %d, T %d)", plan->num_q_heads,
                   plan->num_tokens);
-    if (plan->num_work < 1 || !work_dev) return fail(FG_E_ARG, "empty or null work list");
+    if (plan->num_work < 1 || !work_dev || plan->num_groups < 0 ||
+        plan->num_groups >= plan->num_work)
+      return fail(FG_E_ARG, "empty, null or inconsistent work list");
     if (plan->workspace_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan->workspace_bytes))
       return fail(FG_E_WORKSPACE, "workspace of %zu bytes, plan needs %lld", workspace_bytes,
                   (long long)plan->workspace_bytes);
@@ -789,7 +803,6 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
     P.v_pool = (const u16 *)cache->v_pool;
     P.out = (u16 *)out;
     P.ws = (float *)workspace;
-    P.counters = (int32_t *)workspace;
     P.ws_floats = (int64_t)(workspace ? workspace_bytes / 4 : 0);
     P.Hq = num_q_heads;
     P.Hkv = c.num_kv_heads;
@@ -798,7 +811,14 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
     P.bs_log2 = cache->bs_log2;
     P.num_blocks = c.num_blocks;
     P.sl2 = scale * LOG2E;
-    hipLaunchKernelGGL(attention_bf16_kernel, dim3(plan->num_work), dim3(NT), 0, st, P);
+    const int32_t main_records = plan->num_work - plan->num_groups;
+    if (c.block_size >= KT)
+      hipLaunchKernelGGL(attention_bf16_kernel<true>, dim3(main_records), dim3(NT), 0, st, P);
+    else
+      hipLaunchKernelGGL(attention_bf16_kernel<false>, dim3(main_records), dim3(NT), 0, st, P);
+    if (plan->num_groups > 0)
+      hipLaunchKernelGGL(attention_combine_kernel, dim3(plan->num_groups), dim3(NT), 0, st, P,
+                         main_records);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_E_HIP, "attention launch: %s", hipGetErrorString(e));

@@ -54,7 +54,7 @@ class FgRaggedBatch(ctypes.Structure):
 
 class FgPlanInfo(ctypes.Structure):
     _fields_ = [("num_work", ctypes.c_int32), ("num_groups", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_int64), ("counter_bytes", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64),
                 ("num_q_heads", ctypes.c_int32), ("num_tokens", ctypes.c_int32)]
 
 
@@ -93,21 +93,21 @@ def _declare(L):
     """
     st, vp = ctypes.c_int, ctypes.c_void_p
     sigs = {
-        "fg_blocked_cache_init": ([ctypes.POINTER(FgCacheConfig), vp, vp, i32p, ctypes.c_int32,
+        "fg_blocked_cache_init": ([ctypes.POINTER(FgCacheConfig), vp, vp, vp, ctypes.c_int32,
                                    ctypes.POINTER(vp)], st),
         "fg_blocked_cache_destroy": ([vp], st),
         "fg_blocked_cache_num_free": ([vp], ctypes.c_int32),
-        "fg_blocked_cache_free_ids": ([vp, i32p, ctypes.c_int32, i32p], st),
-        "fg_blocked_cache_release": ([vp, i32p, ctypes.c_int32], st),
+        "fg_blocked_cache_free_ids": ([vp, vp, ctypes.c_int32, i32p], st),
+        "fg_blocked_cache_release": ([vp, vp, ctypes.c_int32], st),
         "fg_splitfuse_compose": ([vp, ctypes.POINTER(FgSeqState), ctypes.c_int32, ctypes.c_int32,
                                   ctypes.POINTER(FgRaggedBatch)], st),
         "fg_splitfuse_commit": ([ctypes.POINTER(FgSeqState), ctypes.c_int32], st),
         "fg_validate_batch": ([vp, ctypes.POINTER(FgRaggedBatch)], st),
         "fg_kv_append": ([vp, ctypes.POINTER(FgRaggedBatch), vp, vp, vp], st),
         "fg_attention_plan": ([vp, ctypes.POINTER(FgRaggedBatch), ctypes.c_int32, ctypes.c_int32,
-                               ctypes.POINTER(FgPlanInfo), i32p, ctypes.c_int32], st),
+                               ctypes.POINTER(FgPlanInfo), vp, ctypes.c_int32], st),
         "fg_ragged_attention": ([vp, ctypes.POINTER(FgRaggedBatch), ctypes.POINTER(FgPlanInfo),
-                                 i32p, vp, ctypes.c_int32, ctypes.c_float, vp, vp,
+                                 vp, vp, ctypes.c_int32, ctypes.c_float, vp, vp,
                                  ctypes.c_size_t, vp], st),
         "fg_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "fg_last_error": ([], ctypes.c_char_p),
@@ -134,10 +134,19 @@ def _check(status: int, ok=(FG_OK,)):
 
 
 def _ptr(a: np.ndarray | None, ctype=ctypes.c_int32):
+    """Typed pointer to a numpy array (for struct fields; slow-ish, use at setup)."""
     if a is None:
         return None
     assert a.flags["C_CONTIGUOUS"]
-    return a.ctypes.data_as(ctypes.POINTER(ctype))
+    return ctypes.cast(_addr(a), ctypes.POINTER(ctype))
+
+
+def _addr(a: np.ndarray | None):
+    """Address of a contiguous numpy array, cheap enough for per-call marshalling."""
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.__array_interface__["data"][0]
 
 
 # ---- cache handle ---------------------------------------------------------------------
@@ -151,7 +160,7 @@ def fg_blocked_cache_init(num_blocks, block_size, num_kv_heads, head_dim, dtype,
                                            ctypes.byref(h)))
     else:
         ids = np.ascontiguousarray(free_ids, dtype=np.int32)
-        _check(lib().fg_blocked_cache_init(ctypes.byref(cfg), k_pool_ptr, v_pool_ptr, _ptr(ids),
+        _check(lib().fg_blocked_cache_init(ctypes.byref(cfg), k_pool_ptr, v_pool_ptr, _addr(ids),
                                            len(ids), ctypes.byref(h)))
     return h
 
@@ -168,13 +177,13 @@ def fg_blocked_cache_free_ids(handle) -> np.ndarray:
     n = ctypes.c_int32()
     _check(lib().fg_blocked_cache_free_ids(handle, None, 0, ctypes.byref(n)))
     out = np.zeros(n.value, np.int32)
-    _check(lib().fg_blocked_cache_free_ids(handle, _ptr(out), n.value, ctypes.byref(n)))
+    _check(lib().fg_blocked_cache_free_ids(handle, _addr(out), n.value, ctypes.byref(n)))
     return out
 
 
 def fg_blocked_cache_release(handle, blocks):
     b = np.ascontiguousarray(blocks, dtype=np.int32)
-    _check(lib().fg_blocked_cache_release(handle, _ptr(b), len(b)))
+    _check(lib().fg_blocked_cache_release(handle, _addr(b), len(b)))
 
 
 # ---- sequences and batches (host side) -------------------------------------------------
@@ -198,7 +207,7 @@ class SeqStates:
             a.prompt_len = s.prompt_len
             a.n_blocks = nb
             a.max_blocks = per_seq[i]
-            a.blocks = self.blocks[i].ctypes.data_as(i32p)
+            a.blocks = ctypes.cast(_addr(self.blocks) + i * self.blocks.strides[0], i32p)
             a.n_scheduled = 0
 
     def n_cached(self, i):
@@ -251,14 +260,23 @@ def fg_validate_batch(handle, batch: HostBatch):
     _check(lib().fg_validate_batch(handle, ctypes.byref(batch.c)))
 
 
-def fg_attention_plan(handle, batch: HostBatch, num_q_heads: int, num_cus: int):
-    """Returns (FgPlanInfo, work records as an int32 array [num_work][FG_WORK_INTS])."""
+def fg_attention_plan(handle, batch: HostBatch, num_q_heads: int, num_cus: int, work=None):
+    """Returns (FgPlanInfo, work records as an int32 array [num_work][FG_WORK_INTS]).
+
+    ``work`` may be a reusable int32 [capacity][FG_WORK_INTS] buffer; the returned records
+    are a view of it when it is large enough (one call), else a new array (two calls)."""
     info = FgPlanInfo()
-    _check(lib().fg_attention_plan(handle, ctypes.byref(batch.c), int(num_q_heads), int(num_cus),
-                                   ctypes.byref(info), None, 0))
+    cap = 0 if work is None else int(work.shape[0])
+    st = lib().fg_attention_plan(handle, ctypes.byref(batch.c), int(num_q_heads), int(num_cus),
+                                 ctypes.byref(info), _addr(work) if cap else None, cap)
+    if st == FG_OK and info.num_work <= cap:
+        return info, (work[:info.num_work] if work is not None
+                      else np.zeros((0, FG_WORK_INTS), np.int32))
+    if st not in (FG_OK, FG_E_ARG) or info.num_work <= cap:
+        _check(st)
     work = np.zeros((max(info.num_work, 1), FG_WORK_INTS), np.int32)
     _check(lib().fg_attention_plan(handle, ctypes.byref(batch.c), int(num_q_heads), int(num_cus),
-                                   ctypes.byref(info), _ptr(work), info.num_work))
+                                   ctypes.byref(info), _addr(work), info.num_work))
     return info, work[:info.num_work]
 
 
@@ -271,6 +289,6 @@ def fg_kv_append(handle, dev: FgRaggedBatch, k_new_ptr, v_new_ptr, stream):
 def fg_ragged_attention(handle, dev: FgRaggedBatch, info: FgPlanInfo, work_dev_ptr, q_ptr,
                         num_q_heads, scale, out_ptr, workspace_ptr, workspace_bytes, stream):
     _check(lib().fg_ragged_attention(handle, ctypes.byref(dev), ctypes.byref(info),
-                                     ctypes.cast(work_dev_ptr or 0, i32p), q_ptr,
+                                     work_dev_ptr or None, q_ptr,
                                      int(num_q_heads), float(scale), out_ptr, workspace_ptr,
                                      int(workspace_bytes), stream))

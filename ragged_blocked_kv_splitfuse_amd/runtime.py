@@ -4,8 +4,8 @@
 * ``DeviceDescriptors`` — uploads a composed batch and its work list to the device in one
   copy from a ring of pinned staging buffers (an event guards each buffer, so the host can
   compose the next pass while the previous copy is still queued);
-* ``Workspace``         — zero-initialised device scratch for split-key partials; the kernel
-  leaves its counter region zero after every call, so it is cleared only when it grows.
+* ``Workspace``         — device scratch for split-key partials (no initialisation needed),
+  grown on demand.
 
 No arithmetic of the method happens here.
 """
@@ -132,5 +132,5 @@ class Workspace:
         if nbytes <= 0:
             return 0, 0
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(int(nbytes), dtype=torch.uint8, device=self.device)
+            self.buf = torch.empty(int(nbytes), dtype=torch.uint8, device=self.device)
         return self.buf.data_ptr(), self.buf.numel()

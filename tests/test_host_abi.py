@@ -287,13 +287,14 @@ def _compose_c(w, budget=None):
 def check_plan(hb, info, work, hq, hkv, head_dim=128):
     G = hq // hkv
     S = hb.num_seqs
-    assert info.num_work == len(work)
+    assert info.num_work == len(work) and 0 <= info.num_groups < max(info.num_work, 1)
+    main, merges = work[:info.num_work - info.num_groups], work[info.num_work - info.num_groups:]
     slot = {0: 16 * (head_dim + 2), 1: 128 * (head_dim + 2)}
     groups = {}
     cover = {}
-    for rec in work:
+    for rec in main:
         s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff, _ = (int(x) for x in rec)
-        assert 0 <= s < S and 0 <= h < hkv and nt >= 1
+        assert 0 <= s < S and 0 <= h < hkv and nt >= 1 and sp >= 0
         assert mode == (0 if nt * G <= 16 else 1) and nt * G <= 128
         c, n = int(hb.context_len[s]), int(hb.n_query[s])
         assert 0 <= t0 and t0 + nt <= n
@@ -309,7 +310,7 @@ def check_plan(hb, info, work, hq, hkv, head_dim=128):
                 assert t0 == pos
                 pos += nt
             assert pos == int(hb.n_query[s])
-    # split groups partition the key range in split order; partial slots disjoint
+    # split groups partition the key range in split order; partial slots are disjoint
     spans = []
     for (s, h, t0, nt), recs in cover.items():
         c = int(hb.context_len[s])
@@ -318,8 +319,8 @@ def check_plan(hb, info, work, hq, hkv, head_dim=128):
             assert recs[0][0] == 0 and recs[0][1] == c + t0 + nt
             continue
         grp, nsp, poff, mode = recs[0][2], recs[0][4], recs[0][5], recs[0][6]
-        assert grp >= 0 and len(recs) == nsp and grp not in groups
-        groups[grp] = True
+        assert grp >= 0 and len(recs) == nsp > 1 and grp not in groups
+        groups[grp] = (s, h, t0, nt, mode, nsp, poff)
         assert [r[3] for r in recs] == list(range(nsp))
         assert recs[0][0] == 0 and recs[-1][1] == c + t0 + nt
         for a, b in zip(recs, recs[1:]):
@@ -331,8 +332,13 @@ def check_plan(hb, info, work, hq, hkv, head_dim=128):
     for a, b in zip(spans, spans[1:]):
         assert a[1] <= b[0]
     if spans:
-        assert spans[0][0] * 4 >= info.counter_bytes >= info.num_groups * 4
-        assert spans[-1][1] * 4 <= info.workspace_bytes
+        assert spans[0][0] >= 0 and spans[-1][1] * 4 <= info.workspace_bytes
+    # one merge record per group, in group order, naming the group's rows and slots
+    assert len(merges) == info.num_groups
+    for g, rec in enumerate(merges):
+        s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff, _ = (int(x) for x in rec)
+        assert grp == g and sp == -1
+        assert groups[g] == (s, h, t0, nt, mode, nsp, poff)
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 5])
@@ -381,4 +387,27 @@ def test_plan_errors():
     st = fg.lib().fg_attention_plan(h, ctypes.byref(hb.c), 32, 256, ctypes.byref(info),
                                     work.ctypes.data_as(fg.i32p), 1)
     assert st == fg.FG_E_ARG and info.num_work > 1                            # capacity
+    fg.fg_blocked_cache_destroy(h)
+
+
+def test_plan_fp32_needs_no_records():
+    w = wl.make(1)
+    h, ss, hb = _compose_c(w)
+    for buf in (None, np.zeros((8, fg.FG_WORK_INTS), np.int32)):
+        info, work = fg.fg_attention_plan(h, hb, w.num_q_heads, 256, buf)
+        assert info.num_work == 0 and work.shape == (0, fg.FG_WORK_INTS)
+        assert info.num_tokens == hb.num_tokens and info.workspace_bytes == 0
+    fg.fg_blocked_cache_destroy(h)
+
+
+def test_plan_reuses_a_large_enough_buffer():
+    w = wl.make(2)
+    h, ss, hb = _compose_c(w)
+    info0, work0 = fg.fg_attention_plan(h, hb, 32, 256)
+    buf = np.zeros((info0.num_work + 5, fg.FG_WORK_INTS), np.int32)
+    info1, work1 = fg.fg_attention_plan(h, hb, 32, 256, buf)
+    assert work1.base is buf and np.array_equal(work0, work1)
+    small = np.zeros((3, fg.FG_WORK_INTS), np.int32)
+    info2, work2 = fg.fg_attention_plan(h, hb, 32, 256, small)
+    assert np.array_equal(work0, work2)
     fg.fg_blocked_cache_destroy(h)
