@@ -165,7 +165,7 @@ fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const 
 /* Splits the attention of a host batch into work records (host only).  Sequences with at
  * most 16 query rows (rows = tokens x query heads per KV head) become key-streaming
  * records, others become tiles of up to 128 rows; long key ranges are split so that about
- * num_cus * 4 records' worth of work exists, and records come longest first.  Each split
+ * num_cus * 2 records' worth of work exists, and records come longest first.  Each split
  * group also gets a merge record after all attention records.  Writes the num_work records
  * of FG_WORK_INTS int32 into `work` (host) and fills *info; with work_capacity 0 it only
  * sizes (FG_OK), with 0 < work_capacity < num_work it returns FG_E_ARG.  The caller copies

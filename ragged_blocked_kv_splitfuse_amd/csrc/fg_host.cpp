@@ -339,7 +339,9 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
   }
   double total = 0;
   for (auto &it : base) total += (double)it.cost * Hkv;
-  const double target = total / (4.0 * num_cus);
+  // aim for about two records per compute unit: one full wave of resident workgroups; finer
+  // splits cost partial-result traffic and merge work
+  const double target = total / (2.0 * num_cus);
   const int32_t min_tiles = 4;  // a split covers at least 4 key tiles (256 keys)
 
   std::vector<PlanItem> &items = cache->plan_items;  // one entry per shape and split

@@ -73,7 +73,44 @@ __device__ __forceinline__ uint4 keep_first(uint4 v, int n) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max over the four lanes l, l^16, l^32, l^48 (the lanes that hold one query row in the
+// 16x16 MFMA result layout), with the gfx950 lane-swap instructions instead of LDS permutes.
+// v_permlane16_swap applied to two copies of x leaves {x[l], x[l^16]} in the two registers of
+// every lane (16-lane rows 0<->1 and 2<->3 trade places); v_permlane32_swap does the same for
+// l^32.  Written as one asm block: through the builtins the compiler treated the swap of two
+// equal values as a no-op and dropped the max that follows.  The s_nop gives the swap the two
+// wait states it needs after a VALU write of its operands.
+__device__ __forceinline__ float row_max4(float x) {
+  float t;
+  asm volatile(
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane16_swap_b32 %0, %1\n\t"
+      "v_max_f32 %0, %0, %1\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(x), "=&v"(t));
+  return x;
+}
+
+// The running max used for the exponentials is only moved when a row's new max exceeds it
+// by more than LAZY_TAU (log2 units).  Softmax does not depend on the shift, so this is exact
+// in exact arithmetic; it bounds p by 2^LAZY_TAU and spares the accumulator rescale on most
+// key tiles.
+constexpr float LAZY_TAU = 8.f;
+
 __device__ __forceinline__ int clamp_block(int b, int nb) { return b < 0 ? 0 : (b >= nb ? nb - 1 : b); }
+
+// Descriptors, block tables and work records are read-only while a kernel runs.  Reading them
+// through the constant address space lets wave-uniform reads become scalar loads, which are
+// counted apart from the vector loads still in flight (a vector read of a block id would make
+// its wait drain every outstanding tile load as well).
+typedef __attribute__((address_space(4))) const int32_t cint32_t;
+__device__ __forceinline__ int ldc(const int32_t *p, size_t i) {
+  return ((cint32_t *)p)[i];
+}
 
 // Swizzles of the LDS tiles (16-byte chunk index XOR a row function) that make the MFMA
 // operand reads and the cooperative tile writes free of bank conflicts.
@@ -104,17 +141,17 @@ struct Rec {
 
 __device__ __forceinline__ Rec load_rec(const int32_t *w) {
   Rec r;
-  r.s = w[W_SEQ];
-  r.h = w[W_KVH];
-  r.tok0 = w[W_TOK0];
-  r.ntok = w[W_NTOK];
-  r.klo = w[W_KLO];
-  r.khi = w[W_KHI];
-  r.mode = w[W_MODE];
-  r.group = w[W_GROUP];
-  r.split = w[W_SPLIT];
-  r.nsplit = w[W_NSPLIT];
-  r.poff = w[W_POFF];
+  r.s = ldc(w, W_SEQ);
+  r.h = ldc(w, W_KVH);
+  r.tok0 = ldc(w, W_TOK0);
+  r.ntok = ldc(w, W_NTOK);
+  r.klo = ldc(w, W_KLO);
+  r.khi = ldc(w, W_KHI);
+  r.mode = ldc(w, W_MODE);
+  r.group = ldc(w, W_GROUP);
+  r.split = ldc(w, W_SPLIT);
+  r.nsplit = ldc(w, W_NSPLIT);
+  r.poff = ldc(w, W_POFF);
   return r;
 }
 
@@ -158,9 +195,9 @@ __device__ __forceinline__ void online_softmax(f32x4 (&s)[2][2], bool need_mask,
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[kh][a][j]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float m_new = fmaxf(m, mx * sl2);
+  mx = row_max4(mx) * sl2;
+  const bool upd = mx > m + LAZY_TAU;
+  const float m_new = upd ? mx : m;
   const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
   const float alpha = fast_exp2(m - m_use);
   float psum = 0.f;
@@ -177,7 +214,7 @@ __device__ __forceinline__ void online_softmax(f32x4 (&s)[2][2], bool need_mask,
       }
   l = l * alpha + psum;
   m = m_new;
-  if (__ballot(alpha != 1.f)) {
+  if (__ballot(upd)) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
   }
@@ -185,15 +222,61 @@ __device__ __forceinline__ void online_softmax(f32x4 (&s)[2][2], bool need_mask,
   pf[1] = to_bf16x8(p[1]);
 }
 
+// The same step for a 32-key stage: s[a][j] is the score of key key0 + 4a + j.
+__device__ __forceinline__ void online_softmax32(f32x4 (&s)[2], bool need_mask, int key0,
+                                                 int lim, int khi, float sl2, float &m, float &l,
+                                                 f32x4 *acc, bf16x8 &pf) {
+  if (need_mask) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = key0 + 4 * a + j;
+        if (key > lim || key >= khi) s[a][j] = NEG_INF;
+      }
+  }
+  float mx = NEG_INF;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[a][j]);
+  mx = row_max4(mx) * sl2;
+  const bool upd = mx > m + LAZY_TAU;
+  const float m_new = upd ? mx : m;
+  const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+  const float alpha = fast_exp2(m - m_use);
+  float p[8], psum = 0.f;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = fast_exp2(fmaf(s[a][j], sl2, -m_use));
+      p[4 * a + j] = e;
+      psum += e;
+    }
+  l = l * alpha + psum;
+  m = m_new;
+  if (__ballot(upd)) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
+  }
+  pf = to_bf16x8(p);
+}
+
+constexpr int MERGE_ROWS = NT / (D / 8);  // rows one merge workgroup covers (16)
+
 // Combine: the merge record of a split group reads every split's (m, l, acc) partial in
 // split order (deterministic) and writes O.  Runs in its own launch after the main kernel.
+// Each workgroup merges one 16-row slice (blockIdx.y) of the group: one thread per (row,
+// 8-feature chunk).
 __device__ void merge_splits(const Params &P, const Rec &R) {
   const int64_t slot = slot_floats(R.mode, D);
   const int cap = R.mode == MODE_STREAM ? STREAM_ROWS : TILE_ROWS;
   const int rows = R.ntok * P.G;
-  const int qs = P.query_start[R.s];
-  for (int idx = threadIdx.x; idx < rows * (D / 8); idx += NT) {
-    const int row = idx / (D / 8), chunk = idx % (D / 8);
+  const int qs = ldc(P.query_start, R.s);
+  {
+    const int row = MERGE_ROWS * blockIdx.y + threadIdx.x / (D / 8), chunk = threadIdx.x % (D / 8);
+    if (row >= rows) return;
     float M = NEG_INF;
     for (int k = 0; k < R.nsplit; ++k) M = fmaxf(M, P.ws[R.poff + k * slot + cap * D + row]);
     float L = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -218,7 +301,7 @@ __device__ void merge_splits(const Params &P, const Rec &R) {
 // keys past the sequence end still sit inside an allocated block.
 template <bool BIG>
 __device__ __forceinline__ int tile_block(const Params &P, const int32_t *bt, int k0) {
-  return BIG ? clamp_block(bt[k0 >> P.bs_log2], P.num_blocks) : 0;
+  return BIG ? clamp_block(ldc(bt, k0 >> P.bs_log2), P.num_blocks) : 0;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -226,11 +309,11 @@ __device__ __forceinline__ int tile_block(const Params &P, const int32_t *bt, in
 // from HBM into MFMA operand registers (no LDS staging, no barriers), then the four waves
 // merge their running states through LDS.
 // ---------------------------------------------------------------------------------------
-template <bool BIG>
-__device__ void stream_record(const Params &P, const Rec &R, unsigned char *smem) {
+template <bool BIG, typename LdsT>
+__device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
-  const int c = P.context_len[R.s], qs = P.query_start[R.s];
-  const int L = c + P.n_query[R.s];
+  const int c = ldc(P.context_len, R.s), qs = ldc(P.query_start, R.s);
+  const int L = c + ldc(P.n_query, R.s);
   const int rows = R.ntok * P.G;
   const int32_t *bt = P.block_table + (size_t)R.s * P.table_stride;
   const int bs_mask = P.bs - 1;
@@ -317,13 +400,15 @@ __device__ void stream_record(const Params &P, const Rec &R, unsigned char *smem
   l_run += __shfl_xor(l_run, 32, 64);
 
   // ---- merge the four waves through LDS ------------------------------------------------
-  constexpr int OP = D + 4;  // padded row of the per-wave O^T dump
-  float *so = reinterpret_cast<float *>(smem);                 // [NW][16][OP]
-  float *sm = so + NW * STREAM_ROWS * OP;                      // [NW][16]
+  // per-wave O^T dumps: wave w uses the K half of stage buffer w (8 KiB = 16 rows x 128);
+  // a select chain keeps every LDS address tied to a fixed array
+  float *so_w = reinterpret_cast<float *>(w == 0 ? S.st[0] : w == 1 ? S.st[1]
+                                          : w == 2 ? S.st[2] : S.st[3]);
+  float *sm = reinterpret_cast<float *>(S.vs[0]);              // [NW][16]
   float *sl = sm + NW * STREAM_ROWS;                           // [NW][16]
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
-    *reinterpret_cast<f32x4 *>(so + (w * STREAM_ROWS + r) * OP + 16 * dt + 4 * g) = acc[dt];
+    *reinterpret_cast<f32x4 *>(so_w + r * D + 16 * dt + 4 * g) = acc[dt];
   if (g == 0) {
     sm[w * STREAM_ROWS + r] = m_run;
     sl[w * STREAM_ROWS + r] = l_run;
@@ -340,7 +425,7 @@ __device__ void stream_record(const Params &P, const Rec &R, unsigned char *smem
     const float m = sm[ww * STREAM_ROWS + row];
     const float f = (m == NEG_INF) ? 0.f : fast_exp2(m - M);
     Lsum += sl[ww * STREAM_ROWS + row] * f;
-    const float *src = so + (ww * STREAM_ROWS + row) * OP + chunk * 8;
+    const float *src = reinterpret_cast<const float *>(S.st[ww]) + row * D + chunk * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] += src[i] * f;
   }
@@ -360,25 +445,125 @@ __device__ void stream_record(const Params &P, const Rec &R, unsigned char *smem
 
 // ---------------------------------------------------------------------------------------
 // MODE_TILE: up to 128 query rows (chunk rows).  Wave w owns rows [32w, 32w+32) as two
-// 16-row MFMA tiles; each 64-key K/V tile is gathered cooperatively (coalesced 16-byte
-// loads through the block table) into double-buffered, swizzled LDS and shared by all waves.
+// 16-row MFMA tiles.  Keys advance in 32-key stages; each stage's K [32 keys][128] and
+// V^T [128][32 keys] are fetched straight from HBM into LDS (global_load_lds_dwordx4, no
+// register staging) through a ring of NSTAGE buffers, NSTAGE-1 stages ahead of the math, so
+// the load latency hides behind three stages of MFMA work.  Every lane's source address is
+// chosen so that the 1 KiB each wave instruction writes contiguously lands already swizzled.
 // ---------------------------------------------------------------------------------------
-constexpr int KTILE_ELEMS = KT * D;   // K tile [64 keys][128]
-constexpr int VTILE_ELEMS = D * KT;   // V^T tile [128 features][64 keys]
-constexpr int BUF_ELEMS = KTILE_ELEMS + VTILE_ELEMS;
+constexpr int KS = 32;                     // keys per stage
+constexpr int NSTAGE = 4;                  // ring depth
+constexpr int STAGE_K = KS * D;            // u16 elements of the K part of a stage
+constexpr int STAGE_ELEMS = 2 * KS * D;    // K + V^T: 16 KiB (two 8 KiB arrays)
+static_assert(STREAM_ROWS * D * 4 <= STAGE_K * 2, "a wave's stream dump must fit a K array");
 
-template <bool BIG>
-__device__ void tile_record(const Params &P, const Rec &R, unsigned char *smem) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r = lane & 15;
-  const int c = P.context_len[R.s], qs = P.query_start[R.s];
-  const int L = c + P.n_query[R.s];
-  const int rows = R.ntok * P.G;
-  const int32_t *bt = P.block_table + (size_t)R.s * P.table_stride;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+__device__ __forceinline__ int swz_k32(int key) { return ((key >> 1) & 12) | (key & 3); }
+__device__ __forceinline__ int swz_v32(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
+
+struct Lds {
+  u16 *st[NSTAGE];
+  u16 *vs[NSTAGE];
+};
+
+__device__ __forceinline__ void dma16(const u16 *src, u16 *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)lds_wave_base, 16, 0, 0);
+}
+
+// Workgroup barrier for the stage ring.  __syncthreads() would also drain every vector load
+// still in flight (its fence waits for all of them), i.e. the prefetched stages; here the
+// data a stage needs is already covered by wait_dma, and LDS reads complete before their
+// MFMAs consume them, so a bare barrier suffices.  The empty asm statements keep the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// wait until at most n of this wave's LDS-DMA loads are outstanding (n in {0, 4, 8})
+__device__ __forceinline__ void wait_dma(int n) {
+  // s_waitcnt encoding (gfx9): vmcnt = bits 3:0 (+15:14), expcnt 6:4, lgkmcnt 11:8
+  if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+  else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Per-lane parts of the four LDS-DMA source addresses of a stage (bytes from the stage's
+// first key in its block), constant over a record when a stage lies inside one block.
+struct DmaOffsets {
+  uint32_t k[2], v[2];
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets(int bs) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  DmaOffsets o;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int reg = 2 * w + p;
+    // K: region `reg` holds key rows 4*reg .. 4*reg+3; lane -> (key row, 16-byte slot)
+    const int keyl = 4 * reg + (lane >> 4), ch = (lane & 15) ^ swz_k32(keyl);
+    o.k[p] = (uint32_t)(keyl * D + 8 * ch) * 2u;
+    // V^T: region `reg` holds feature rows 16*reg .. +15; lane -> (row, 8-key slot)
+    const int d = 16 * reg + (lane >> 2), kc = (lane & 3) ^ swz_v32(d);
+    o.v[p] = (uint32_t)(d * bs + 8 * kc) * 2u;
+  }
+  return o;
+}
+
+template <int BSC>
+__device__ __forceinline__ void issue_stage(const Params &P, const Rec &R, const int32_t *bt,
+                                            int L, int k0, const DmaOffsets &o, u16 *buf,
+                                            u16 *vbuf) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int bs_mask = P.bs - 1;
   const size_t head_stride = (size_t)P.bs * D;
-  u16 *lds = reinterpret_cast<u16 *>(smem);
+  if (BSC >= 1) {
+    // a 32-key stage lies in one block: uniform base + per-lane offset
+    const int blk = clamp_block(ldc(bt, k0 >> P.bs_log2), P.num_blocks);
+    const size_t hb = ((size_t)blk * P.Hkv + R.h) * head_stride;
+    const char *kb = reinterpret_cast<const char *>(P.k_pool + hb + (size_t)(k0 & bs_mask) * D);
+    const char *vb = reinterpret_cast<const char *>(P.v_pool + hb + (k0 & bs_mask));
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      dma16(reinterpret_cast<const u16 *>(kb + o.k[p]), buf + (2 * w + p) * 512);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      dma16(reinterpret_cast<const u16 *>(vb + o.v[p]), vbuf + (2 * w + p) * 512);
+    return;
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int reg = 2 * w + p;
+    const int keyl = 4 * reg + (lane >> 4), ch = (lane & 15) ^ swz_k32(keyl);
+    const int key = min(k0 + keyl, L - 1);
+    const int blk = clamp_block(bt[key >> P.bs_log2], P.num_blocks);
+    dma16(P.k_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)(key & bs_mask) * D + 8 * ch,
+          buf + reg * 512);
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int reg = 2 * w + p;
+    const int d = 16 * reg + (lane >> 2), kc = (lane & 3) ^ swz_v32(d);
+    const int key0 = min(k0 + 8 * kc, (L - 1) & ~7);
+    const int blk = clamp_block(bt[key0 >> P.bs_log2], P.num_blocks);
+    dma16(P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)d * P.bs + (key0 & bs_mask),
+          vbuf + reg * 512);
+  }
+}
 
-  const int nrt = rows > 32 * w ? (rows > 32 * w + 16 ? 2 : 1) : 0;
+template <int BSC>
+__device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r = lane & 15;
+  const int c = ldc(P.context_len, R.s), qs = ldc(P.query_start, R.s);
+  const int L = c + ldc(P.n_query, R.s);
+  const int rows = R.ntok * P.G;
+  const int32_t *bt = P.block_table + (size_t)R.s * P.table_stride;
+
+  // row tiles this wave owns (wave-uniform, so its branches stay scalar)
+  const int nrt = __builtin_amdgcn_readfirstlane(rows > 32 * w ? (rows > 32 * w + 16 ? 2 : 1) : 0);
   bf16x8 qf[2][D / 32];
   int lim[2];
 #pragma unroll
@@ -400,114 +585,82 @@ __device__ void tile_record(const Params &P, const Rec &R, unsigned char *smem) 
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) acc[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // cooperative tile load: K chunk q -> (key q>>4, 16-byte chunk q&15);
-  //                        V chunk q -> (feature q>>3, 8-key chunk q&7)
-  uint4 kreg[4], vreg[4];
-  auto gload = [&](int kt) {
-    const int k0 = kt * KT;
-    const int blk_t = tile_block<BIG>(P, bt, k0);
-    const u16 *kb = P.k_pool + ((size_t)blk_t * P.Hkv + R.h) * head_stride + (size_t)(k0 & bs_mask) * D;
-    const u16 *vb = P.v_pool + ((size_t)blk_t * P.Hkv + R.h) * head_stride + (k0 & bs_mask);
+  const int s_begin = R.klo / KS, s_end = (R.khi + KS - 1) / KS, nst = s_end - s_begin;
+  const DmaOffsets doff = dma_offsets(P.bs);
+  // prologue: stages 0 .. NSTAGE-2 in flight
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int qi = tid + NT * p;
-      if (BIG) {
-        kreg[p] = ld16(kb + (size_t)(qi >> 4) * D + 8 * (qi & 15));
-      } else {
-        const int key = min(k0 + (qi >> 4), L - 1);
-        const int blk = clamp_block(bt[key >> P.bs_log2], P.num_blocks);
-        kreg[p] = ld16(P.k_pool + ((size_t)blk * P.Hkv + R.h) * head_stride +
-                       (size_t)(key & bs_mask) * D + 8 * (qi & 15));
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int qi = tid + NT * p;
-      const int d = qi >> 3;
-      const int key0 = k0 + 8 * (qi & 7);
-      uint4 v;
-      if (BIG) {
-        v = ld16(vb + (size_t)d * P.bs + 8 * (qi & 7));
-      } else {
-        const int keyc = min(key0, (L - 1) & ~7);
-        const int blk = clamp_block(bt[keyc >> P.bs_log2], P.num_blocks);
-        v = ld16(P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)d * P.bs +
-                 (keyc & bs_mask));
-      }
-      if (key0 + 8 > R.khi) v = keep_first(v, min(max(R.khi - key0, 0), 8));
-      vreg[p] = v;
-    }
-  };
-  auto swrite = [&](int buf) {
-    u16 *Kl = lds + buf * BUF_ELEMS;
-    u16 *Vl = Kl + KTILE_ELEMS;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int qi = tid + NT * p;
-      const int key = qi >> 4, ch = qi & 15;
-      *reinterpret_cast<uint4 *>(Kl + key * D + 8 * (ch ^ swz_k(key))) = kreg[p];
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int qi = tid + NT * p;
-      const int d = qi >> 3, ch = qi & 7;
-      *reinterpret_cast<uint4 *>(Vl + d * KT + 8 * (ch ^ swz_v(d))) = vreg[p];
-    }
-  };
+  for (int i = 0; i < NSTAGE - 1; ++i)
+    if (i < nst) issue_stage<BSC>(P, R, bt, L, (s_begin + i) * KS, doff, S.st[i], S.vs[i]);
 
-  const int t_begin = R.klo / KT, t_end = (R.khi + KT - 1) / KT;
-  gload(t_begin);
-  swrite(0);
-  __syncthreads();
-  for (int kt = t_begin; kt < t_end; ++kt) {
-    const int buf = (kt - t_begin) & 1;
-    const bool more = kt + 1 < t_end;
-    if (more) gload(kt + 1);
-    if (nrt > 0) {
-      const u16 *Kl = lds + buf * BUF_ELEMS;
-      const u16 *Vl = Kl + KTILE_ELEMS;
-      const int k0 = kt * KT;
-      f32x4 st[2][2][2];
+  for (int base = 0; base < nst; base += NSTAGE) {
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int a = 0; a < 2; ++a) st[rt][kh][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int keyl = 32 * kh + 8 * (r >> 2) + 4 * a + (r & 3);
-          const u16 *kb = Kl + keyl * D;
-          const int sw = swz_k(keyl);
-#pragma unroll
-          for (int dc = 0; dc < D / 32; ++dc) {
-            const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(kb + 8 * ((4 * dc + g) ^ sw)));
-            st[0][kh][a] = mfma_bf16(kf, qf[0][dc], st[0][kh][a]);
-            if (nrt > 1) st[1][kh][a] = mfma_bf16(kf, qf[1][dc], st[1][kh][a]);
-          }
+    for (int u = 0; u < NSTAGE; ++u) {   // unrolled so every stage buffer is a fixed array
+      const int i = base + u;
+      if (i >= nst) break;
+      const int k0 = (s_begin + i) * KS;
+      u16 *buf = S.st[u];
+      wait_dma(4 * min(NSTAGE - 2, nst - 1 - i));  // this wave's loads of stage i landed
+      stage_barrier();                              // ... and every other wave's
+      if (i + NSTAGE - 1 < nst)                     // refill the buffer stage i-1 used
+        issue_stage<BSC>(P, R, bt, L, (s_begin + i + NSTAGE - 1) * KS, doff,
+                         S.st[(u + NSTAGE - 1) % NSTAGE], S.vs[(u + NSTAGE - 1) % NSTAGE]);
+      if (k0 + KS > R.khi) {
+        // keys at or past khi may hold stale bits: zero their V so they cannot reach O
+        u16 *Vl = S.vs[u];
+        for (int idx = tid; idx < D * KS; idx += NT) {
+          const int d = idx / KS, key = idx % KS;
+          if (k0 + key >= R.khi) Vl[d * KS + 8 * ((key >> 3) ^ swz_v32(d)) + (key & 7)] = 0;
         }
-      const bool need_mask = (k0 + KT > R.khi) || (k0 + KT - 1 > c + R.tok0);
-      bf16x8 pf[2][2];
-      online_softmax(st[0], need_mask, k0 + 8 * g, lim[0], R.khi, P.sl2, m_run[0], l_run[0],
-                     acc[0], pf[0]);
-      if (nrt > 1)
-        online_softmax(st[1], need_mask, k0 + 8 * g, lim[1], R.khi, P.sl2, m_run[1], l_run[1],
-                       acc[1], pf[1]);
+        __syncthreads();
+      }
+      if (nrt == 0) continue;
+      const u16 *Kl = buf;
+      const u16 *Vl = S.vs[u];
+      // ---- S^T = K . Q^T for both row tiles, sharing the K operand -------------------
+      bf16x8 kf[2][D / 32];
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+      for (int a = 0; a < 2; ++a) {
+        const int keyl = 8 * (r >> 2) + 4 * a + (r & 3);
+        const int sw = swz_k32(keyl);
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const int d = 16 * dt + r;
-          const bf16x8 vf = as_bf16x8(
-              *reinterpret_cast<const uint4 *>(Vl + d * KT + 8 * ((4 * kh + g) ^ swz_v(d))));
-          acc[0][dt] = mfma_bf16(vf, pf[0][kh], acc[0][dt]);
-          if (nrt > 1) acc[1][dt] = mfma_bf16(vf, pf[1][kh], acc[1][dt]);
-        }
+        for (int dc = 0; dc < D / 32; ++dc)
+          kf[a][dc] = as_bf16x8(*reinterpret_cast<const uint4 *>(Kl + keyl * D + 8 * ((4 * dc + g) ^ sw)));
+      }
+      f32x4 st0[2][2], st1[2][2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        st0[0][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st1[0][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st0[1][a] = st1[1][a] = f32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};  // 2nd half: none
+#pragma unroll
+        for (int dc = 0; dc < D / 32; ++dc) st0[0][a] = mfma_bf16(kf[a][dc], qf[0][dc], st0[0][a]);
+      }
+      if (nrt > 1) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int dc = 0; dc < D / 32; ++dc) st1[0][a] = mfma_bf16(kf[a][dc], qf[1][dc], st1[0][a]);
+      }
+      // V^T operands of this stage (8 consecutive keys of one feature per lane)
+      bf16x8 vf[D / 16];
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const int d = 16 * dt + r;
+        vf[dt] = as_bf16x8(*reinterpret_cast<const uint4 *>(Vl + d * KS + 8 * (g ^ swz_v32(d))));
+      }
+      const bool need_mask = (k0 + KS > R.khi) || (k0 + KS - 1 > c + R.tok0);
+      bf16x8 pf0[2], pf1[2];
+      online_softmax32(st0[0], need_mask, k0 + 8 * g, lim[0], R.khi, P.sl2, m_run[0], l_run[0],
+                       acc[0], pf0[0]);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) acc[0][dt] = mfma_bf16(vf[dt], pf0[0], acc[0][dt]);
+      if (nrt > 1) {
+        online_softmax32(st1[0], need_mask, k0 + 8 * g, lim[1], R.khi, P.sl2, m_run[1],
+                         l_run[1], acc[1], pf1[0]);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) acc[1][dt] = mfma_bf16(vf[dt], pf1[0], acc[1][dt]);
+      }
     }
-    if (more) swrite(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: normalise and store, or write the split partial ------------------------
@@ -548,19 +701,34 @@ __device__ void tile_record(const Params &P, const Rec &R, unsigned char *smem) 
   }
 }
 
-constexpr int SMEM_BYTES = 2 * BUF_ELEMS * 2;  // 64 KiB: two K + V^T tile buffers
-
 // One launch serves every record of the pass: stream records (decode rows, HBM-bound) and
 // tile records (chunk rows, MFMA-bound); the branch is uniform per workgroup.
-template <bool BIG>
+// BSC: 0 = blocks of < 32 keys, 1 = blocks of 32 keys, 2 = blocks of >= 64 keys.
+template <int BSC>
 __global__ __launch_bounds__(NT, 2) void attention_bf16_kernel(Params P) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
+  __shared__ __attribute__((aligned(16))) u16 st0[STAGE_ELEMS / 2];
+  __shared__ __attribute__((aligned(16))) u16 st1[STAGE_ELEMS / 2];
+  __shared__ __attribute__((aligned(16))) u16 st2[STAGE_ELEMS / 2];
+  __shared__ __attribute__((aligned(16))) u16 st3[STAGE_ELEMS / 2];
+  __shared__ __attribute__((aligned(16))) u16 vs0[STAGE_ELEMS / 2];
+  __shared__ __attribute__((aligned(16))) u16 vs1[STAGE_ELEMS / 2];
+  __shared__ __attribute__((aligned(16))) u16 vs2[STAGE_ELEMS / 2];
+  __shared__ __attribute__((aligned(16))) u16 vs3[STAGE_ELEMS / 2];
   const Rec R = load_rec(P.work + (size_t)blockIdx.x * FG_WORK_INTS);
   if (R.s < 0 || !rec_fits_workspace(P, R)) return;  // never write outside the workspace
+  Lds S;
+  S.st[0] = st0;
+  S.st[1] = st1;
+  S.st[2] = st2;
+  S.st[3] = st3;
+  S.vs[0] = vs0;
+  S.vs[1] = vs1;
+  S.vs[2] = vs2;
+  S.vs[3] = vs3;
   if (R.mode == MODE_STREAM)
-    stream_record<BIG>(P, R, smem);
+    stream_record<BSC == 2>(P, R, S);
   else
-    tile_record<BIG>(P, R, smem);
+    tile_record<BSC>(P, R, S);
 }
 
 // Merge records follow the attention records in the work list, one per split group.
@@ -812,12 +980,15 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
     P.num_blocks = c.num_blocks;
     P.sl2 = scale * LOG2E;
     const int32_t main_records = plan->num_work - plan->num_groups;
-    if (c.block_size >= KT)
-      hipLaunchKernelGGL(attention_bf16_kernel<true>, dim3(main_records), dim3(NT), 0, st, P);
+    if (c.block_size >= 64)
+      hipLaunchKernelGGL(attention_bf16_kernel<2>, dim3(main_records), dim3(NT), 0, st, P);
+    else if (c.block_size == 32)
+      hipLaunchKernelGGL(attention_bf16_kernel<1>, dim3(main_records), dim3(NT), 0, st, P);
     else
-      hipLaunchKernelGGL(attention_bf16_kernel<false>, dim3(main_records), dim3(NT), 0, st, P);
+      hipLaunchKernelGGL(attention_bf16_kernel<0>, dim3(main_records), dim3(NT), 0, st, P);
     if (plan->num_groups > 0)
-      hipLaunchKernelGGL(attention_combine_kernel, dim3(plan->num_groups), dim3(NT), 0, st, P,
+      hipLaunchKernelGGL(attention_combine_kernel,
+                         dim3(plan->num_groups, TILE_ROWS / MERGE_ROWS), dim3(NT), 0, st, P,
                          main_records);
   }
   const hipError_t e = hipGetLastError();

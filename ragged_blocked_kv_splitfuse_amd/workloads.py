@@ -64,22 +64,24 @@ class Workload:
     free_ids: np.ndarray = None   # int32, in the order the allocator hands them out
     table_width: int = 0          # block-table row capacity (max blocks per sequence)
     passes: int = 1               # number of consecutive passes the workload asks for
+    q_scale: float = 1.0          # extra factor on Q only (steep-logit stress cases)
 
     # ---- value streams ---------------------------------------------------
-    def _chunk(self, kind: int, seq_id: int, chunk: int, heads: int) -> np.ndarray:
+    def _chunk(self, kind: int, seq_id: int, chunk: int, heads: int, extra: float) -> np.ndarray:
         ss = np.random.SeedSequence([self.seed, kind, seq_id, chunk])
         rng = np.random.Generator(np.random.PCG64(ss))
         x = rng.standard_normal((CHUNK, heads, self.head_dim), dtype=np.float32)
-        if self.value_scale != 1.0:
-            x *= np.float32(self.value_scale)
+        if self.value_scale * extra != 1.0:
+            x *= np.float32(self.value_scale * extra)
         return x
 
-    def _rows(self, kind: int, seq_id: int, p0: int, p1: int, heads: int) -> np.ndarray:
+    def _rows(self, kind: int, seq_id: int, p0: int, p1: int, heads: int,
+              extra: float = 1.0) -> np.ndarray:
         if p1 <= p0:
             shape = (0, heads, self.head_dim)
             return np.zeros(shape, np.uint16 if self.dtype == "bf16" else np.float32)
         c0, c1 = p0 // CHUNK, (p1 + CHUNK - 1) // CHUNK
-        x = np.concatenate([self._chunk(kind, seq_id, c, heads) for c in range(c0, c1)])
+        x = np.concatenate([self._chunk(kind, seq_id, c, heads, extra) for c in range(c0, c1)])
         x = x[p0 - c0 * CHUNK:p1 - c0 * CHUNK]
         return f32_to_bf16_bits(x) if self.dtype == "bf16" else np.ascontiguousarray(x)
 
@@ -92,7 +94,7 @@ class Workload:
 
     def q_rows(self, seq_id: int, p0: int, p1: int) -> np.ndarray:
         """Q rows of positions [p0, p1): [p1-p0][Hq][D]."""
-        return self._rows(KIND_Q, seq_id, p0, p1, self.num_q_heads)
+        return self._rows(KIND_Q, seq_id, p0, p1, self.num_q_heads, self.q_scale)
 
     @property
     def elem_bytes(self) -> int:
@@ -216,7 +218,8 @@ def mistral_gqa(seed: int = 5) -> Workload:
 
 
 def custom(seed, *, dtype="bf16", hq=8, hkv=8, d=128, bs=64, budget=256, n_decode=4,
-           decode_ctx=(64, 600), prompts=((0, 300),), value_scale=1.0, extra_blocks=0):
+           decode_ctx=(64, 600), prompts=((0, 300),), value_scale=1.0, extra_blocks=0,
+           q_scale=1.0):
     """Small mixed workload for parity cases: `n_decode` decodes with contexts uniform in
     `decode_ctx`, then prompts given as (n_cached, prompt_len) pairs, in that order."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -229,6 +232,7 @@ def custom(seed, *, dtype="bf16", hq=8, hkv=8, d=128, bs=64, budget=256, n_decod
     nb = _blocks_upper_bound(specs, bs, budget) + extra_blocks
     w = _finish("custom", dtype, hq, hkv, d, bs, budget, value_scale, seed, specs, nb, rng)
     w.scale = 1.0 / math.sqrt(d)
+    w.q_scale = float(q_scale)
     return w
 
 

@@ -58,6 +58,13 @@ CASES = {
     "gqa3": (dict(hq=12, hkv=4, bs=32, budget=140, n_decode=2, decode_ctx=(50, 200),
                   prompts=((0, 200),)), 256),
     "one_token_fresh": (dict(hq=4, hkv=4, bs=64, budget=1, n_decode=0, prompts=((0, 1),)), 256),
+    # logits with a spread of hundreds: any inconsistency in a row's running max (e.g. a max
+    # taken over only some of the lanes that hold the row) overflows to inf/NaN here
+    "steep_logits": (dict(hq=8, hkv=4, bs=64, budget=300, n_decode=4, decode_ctx=(100, 1500),
+                          prompts=((400, 700),), q_scale=40.0), 256),
+    "steep_logits_split": (dict(hq=4, hkv=4, bs=32, budget=200, n_decode=3,
+                                decode_ctx=(800, 2000), prompts=((1000, 1200),), q_scale=40.0),
+                           100000),
 }
 
 
