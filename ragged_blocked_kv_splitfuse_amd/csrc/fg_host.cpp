@@ -377,7 +377,9 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
       items.push_back(p);
     }
   }
-  // longest first (ties keep their order), so the long-running records start early
+  // Longest first (ties keep their order), so the long-running records start early; and the
+  // two kinds interleaved in proportion, so the workgroups resident on a CU mix MFMA-bound
+  // tile records with HBM-bound stream records instead of queueing all of one kind first.
   std::vector<std::pair<float, int32_t>> &order = cache->plan_order;
   order.resize(items.size());
   for (size_t i = 0; i < items.size(); ++i) order[i] = {-items[i].cost, (int32_t)i};
@@ -395,12 +397,27 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
     return fail(FG_E_ARG, "work capacity %d < %d records", work_capacity, info->num_work);
   }
   if (info->num_work > 0 && !work) return fail(FG_E_ARG, "work is null");
+  // Each item expands to one record per KV head. Records of the two kinds are interleaved in
+  // proportion (Bresenham-style), each kind keeping its longest-first order.
+  std::vector<int32_t> &kinds = cache->plan_kinds;  // tile items, then stream items, in order
+  kinds.clear();
+  for (int pass = 0; pass < 2; ++pass)
+    for (const auto &o : order)
+      if ((items[o.second].mode == MODE_TILE) == (pass == 0)) kinds.push_back(o.second);
+  size_t n_tile_items = 0;
+  while (n_tile_items < kinds.size() && items[kinds[n_tile_items]].mode == MODE_TILE) ++n_tile_items;
+  const int64_t nt = (int64_t)n_tile_items * Hkv, ns = (int64_t)(kinds.size() - n_tile_items) * Hkv;
   int32_t *w = work;
   int32_t *merge = work + n_main * FG_WORK_INTS;  // merge record of group g at merge[g]
-  for (size_t i = 0; i < items.size(); ++i) {
-    const PlanItem &p = items[order[i].second];
+  int64_t it = 0, is = 0, err = 0;
+  for (int64_t k = 0; k < nt + ns; ++k, w += FG_WORK_INTS) {
+    const bool take_tile = is == ns || (it < nt && err <= 0);
+    err += take_tile ? ns : -nt;
+    const int64_t r = take_tile ? it++ : is++;  // record index within its kind
+    const PlanItem &p = items[kinds[(take_tile ? 0 : n_tile_items) + r / Hkv]];
+    const int32_t h = (int32_t)(r % Hkv);
     const int64_t group_bytes = (int64_t)p.nsplit * slot_floats(p.mode, D) * 4;
-    for (int32_t h = 0; h < Hkv; ++h, w += FG_WORK_INTS) {
+    {
       const int32_t g = p.group >= 0 ? p.group + h : -1;
       const int32_t poff = p.group >= 0 ? (int32_t)((p.poff + h * group_bytes) / 4) : 0;
       w[W_SEQ] = p.s;

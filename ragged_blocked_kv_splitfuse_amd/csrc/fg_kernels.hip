@@ -5,12 +5,14 @@
 // rescaling of FlashAttention (DeepSpeed-FastGen paper card by Holmes et al. 2024, "Key
 // points" and "References" 12-13: FlashAttention-derived kernels), over a PagedAttention-style
 // blocked cache (same card, "Key points").  Nothing of those kernels' CUDA design is reused;
-// the layout below is built around CDNA4's 64-lane waves and its 16x16x32 bf16 MFMA.
+// the layout below is built around CDNA4's 64-lane waves and its 16x16x32 (decode rows) and
+// 32x32x16 (chunk rows) bf16 MFMAs.
 //
 // Notation: query row = (new token, query head of the KV head's group); a work record (see
 // fg_internal.h) names one sequence, one KV head, a run of query tokens and a key range.
 //
-// MFMA formulation.  Scores are computed transposed, S^T = K . Q^T, with K as the A operand
+// MFMA formulation (decode rows; the chunk-row variant with 32x32x16 is described at the tile
+// path).  Scores are computed transposed, S^T = K . Q^T, with K as the A operand
 // (16 keys x 32 features per instruction) and Q^T as the B operand (32 features x 16 rows).
 // The 16x16 result leaves lane l with four keys for query row l%16.  Loading the A operand
 // with key rows permuted as 8*(m/4) + 4*a + m%4 (a = which of two 16-key MFMAs) makes lane
@@ -30,6 +32,7 @@ using namespace fgi;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
 namespace {
@@ -43,6 +46,10 @@ constexpr float NEG_INF = -__builtin_inff();
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -87,6 +94,19 @@ __device__ __forceinline__ float row_max4(float x) {
       "s_nop 1\n\t"
       "v_permlane16_swap_b32 %0, %1\n\t"
       "v_max_f32 %0, %0, %1\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(x), "=&v"(t));
+  return x;
+}
+
+// Max over lanes l and l^32 (the two lanes that hold one query row in the 32x32 MFMA result
+// layout): the second half of row_max4.
+__device__ __forceinline__ float pair_max(float x) {
+  float t;
+  asm volatile(
       "v_mov_b32 %1, %0\n\t"
       "s_nop 1\n\t"
       "v_permlane32_swap_b32 %0, %1\n\t"
@@ -220,47 +240,6 @@ __device__ __forceinline__ void online_softmax(f32x4 (&s)[2][2], bool need_mask,
   }
   pf[0] = to_bf16x8(p[0]);
   pf[1] = to_bf16x8(p[1]);
-}
-
-// The same step for a 32-key stage: s[a][j] is the score of key key0 + 4a + j.
-__device__ __forceinline__ void online_softmax32(f32x4 (&s)[2], bool need_mask, int key0,
-                                                 int lim, int khi, float sl2, float &m, float &l,
-                                                 f32x4 *acc, bf16x8 &pf) {
-  if (need_mask) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = key0 + 4 * a + j;
-        if (key > lim || key >= khi) s[a][j] = NEG_INF;
-      }
-  }
-  float mx = NEG_INF;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[a][j]);
-  mx = row_max4(mx) * sl2;
-  const bool upd = mx > m + LAZY_TAU;
-  const float m_new = upd ? mx : m;
-  const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-  const float alpha = fast_exp2(m - m_use);
-  float p[8], psum = 0.f;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float e = fast_exp2(fmaf(s[a][j], sl2, -m_use));
-      p[4 * a + j] = e;
-      psum += e;
-    }
-  l = l * alpha + psum;
-  m = m_new;
-  if (__ballot(upd)) {
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
-  }
-  pf = to_bf16x8(p);
 }
 
 constexpr int MERGE_ROWS = NT / (D / 8);  // rows one merge workgroup covers (16)
@@ -444,12 +423,20 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
 }
 
 // ---------------------------------------------------------------------------------------
-// MODE_TILE: up to 128 query rows (chunk rows).  Wave w owns rows [32w, 32w+32) as two
-// 16-row MFMA tiles.  Keys advance in 32-key stages; each stage's K [32 keys][128] and
-// V^T [128][32 keys] are fetched straight from HBM into LDS (global_load_lds_dwordx4, no
-// register staging) through a ring of NSTAGE buffers, NSTAGE-1 stages ahead of the math, so
+// MODE_TILE: up to 128 query rows (chunk rows).  Wave w owns rows [32w, 32w+32) as one
+// 32-row tile of the 32x32x16 MFMA.  Keys advance in 32-key stages; each stage's K [32 keys]
+// [128] and V^T [128][32 keys] are fetched straight from HBM into LDS (global_load_lds_dwordx4,
+// no register staging) through a ring of NSTAGE buffers, NSTAGE-1 stages ahead of the math, so
 // the load latency hides behind three stages of MFMA work.  Every lane's source address is
 // chosen so that the 1 KiB each wave instruction writes contiguously lands already swizzled.
+//
+// 32x32x16 layouts (k = 8*(l/32) + i for operand element i of lane l): A row m = l%32, B
+// column n = l%32, result element j of lane l = C[8*(j/4) + 4*(l/32) + j%4][l%32].  Scores
+// are S^T = K . Q^T; A row m reads key pi(m), pi swapping bits 2 and 3 of m, which leaves lane
+// l with keys 8*(l/32) + (0..7) in elements 0..7 and 16 + 8*(l/32) + (0..7) in elements 8..15
+// of its query row l%32: exactly the B operands (k = 16 keys each) of O^T += V^T . P^T.  So a
+// row's softmax state lives in two lanes (l, l^32), and all 64 accumulators of a lane belong
+// to one row, one scale factor.
 // ---------------------------------------------------------------------------------------
 constexpr int KS = 32;                     // keys per stage
 constexpr int NSTAGE = 4;                  // ring depth
@@ -460,8 +447,18 @@ static_assert(STREAM_ROWS * D * 4 <= STAGE_K * 2, "a wave's stream dump must fit
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
-__device__ __forceinline__ int swz_k32(int key) { return ((key >> 1) & 12) | (key & 3); }
-__device__ __forceinline__ int swz_v32(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
+// K stage: 16-byte chunk c of key row `key` sits at slot c ^ swz_k32(key).  The MFMA reads of
+// 16 lanes (rows pi(m), m = 16i .. 16i+15, one chunk) then hit 16 distinct slots.
+__device__ __forceinline__ int swz_k32(int key) {
+  return (key & 3) | ((key >> 1) & 4) | ((key << 1) & 8);
+}
+// V^T stage: 8-key chunk kc of feature row d (64 bytes) sits at slot kc ^ swz_v32(d); 16
+// consecutive features at one chunk cover all 16 slots of a 256-byte window set.
+__device__ __forceinline__ int swz_v32(int d) { return (d >> 2) & 3; }
+// pi: A row m of the score product reads physical key pi(m) of the stage (an involution)
+__device__ __forceinline__ int key_perm32(int m) {
+  return (m & ~12) | ((m >> 1) & 4) | ((m << 1) & 8);
+}
 
 struct Lds {
   u16 *st[NSTAGE];
@@ -483,10 +480,12 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// wait until at most n of this wave's LDS-DMA loads are outstanding (n in {0, 4, 8})
+// wait until at most n of this wave's LDS-DMA loads are outstanding (n in {0, 4, .., 16})
 __device__ __forceinline__ void wait_dma(int n) {
   // s_waitcnt encoding (gfx9): vmcnt = bits 3:0 (+15:14), expcnt 6:4, lgkmcnt 11:8
-  if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+  if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt 16: bits 15:14 = 1, 3:0 = 0
+  else if (n >= 12) __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
+  else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
   else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
@@ -554,149 +553,182 @@ __device__ __forceinline__ void issue_stage(const Params &P, const Rec &R, const
   }
 }
 
+// Online softmax over one 32-key stage for this lane's query row: s[j] is the raw score of key
+// key0 + 16*(j/8) + j%8 (key0 = k0 + 8*(l/32)).  Same arithmetic as online_softmax; P comes
+// back as the two B operands of the P.V product.
+__device__ __forceinline__ void online_softmax_t32(f32x16 &s, bool need_mask, int key0, int lim,
+                                                   int khi, float sl2, float &m, float &l,
+                                                   f32x16 *acc, bf16x8 (&pf)[2]) {
+  if (need_mask) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = key0 + 16 * (j / 8) + j % 8;
+      if (key > lim || key >= khi) s[j] = NEG_INF;
+    }
+  }
+  float mx = s[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
+  mx = pair_max(mx) * sl2;
+  const bool upd = mx > m + LAZY_TAU;
+  const float m_new = upd ? mx : m;
+  const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+  const float alpha = fast_exp2(m - m_use);
+  float p[16], psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    p[j] = fast_exp2(fmaf(s[j], sl2, -m_use));
+    psum += p[j];
+  }
+  l = l * alpha + psum;
+  m = m_new;
+  if (__ballot(upd)) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+  }
+  pf[0] = to_bf16x8(p);
+  pf[1] = to_bf16x8(p + 8);
+}
+
 template <int BSC>
 __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
   const int c = ldc(P.context_len, R.s), qs = ldc(P.query_start, R.s);
   const int L = c + ldc(P.n_query, R.s);
   const int rows = R.ntok * P.G;
   const int32_t *bt = P.block_table + (size_t)R.s * P.table_stride;
 
-  // row tiles this wave owns (wave-uniform, so its branches stay scalar)
-  const int nrt = __builtin_amdgcn_readfirstlane(rows > 32 * w ? (rows > 32 * w + 16 ? 2 : 1) : 0);
-  bf16x8 qf[2][D / 32];
-  int lim[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = 32 * w + 16 * rt + r;
-    const int tok = R.tok0 + row / P.G;
-    lim[rt] = c + tok;
+  // this wave's rows [32w, 32w + 32) (wave-uniform quantities, so their branches stay scalar)
+  const bool active = rows > 32 * w;
+  const int last_row = min(rows, 32 * w + 32) - 1;
+  const int wave_lo = c + R.tok0 + (32 * w) / P.G;    // smallest key limit of the wave's rows
+  const int wave_hi = c + R.tok0 + last_row / P.G;    // largest
+  const int row = 32 * w + n;
+  const int tok = R.tok0 + row / P.G;
+  const int lim = c + tok;  // keys 0 .. lim are visible to this lane's row
+  bf16x8 qf[D / 16];
+  {
     const int t = qs + tok, head = R.h * P.G + row % P.G;
     const bool ok = row < rows && t < P.num_tokens;
-    const u16 *qp = P.q + ((size_t)t * P.Hq + head) * D + 8 * g;
+    // rows past the record read token 0 (always present) and are zeroed: unconditional loads
+    // let the compiler see that the wait after the prologue covers them
+    const u16 *qp = P.q + ((size_t)(ok ? t : 0) * P.Hq + (ok ? head : 0)) * D + 8 * g;
 #pragma unroll
-    for (int dc = 0; dc < D / 32; ++dc)
-      qf[rt][dc] = ok ? as_bf16x8(ld16(qp + 32 * dc)) : as_bf16x8(make_uint4(0, 0, 0, 0));
+    for (int st = 0; st < D / 16; ++st) {
+      const uint4 v = ld16(qp + 16 * st);
+      qf[st] = as_bf16x8(ok ? v : make_uint4(0, 0, 0, 0));
+    }
   }
-  float m_run[2] = {NEG_INF, NEG_INF}, l_run[2] = {0.f, 0.f};
-  f32x4 acc[2][D / 16];
+  float m_run = NEG_INF, l_run = 0.f;
+  f32x16 acc[D / 32];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) acc[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+
+  // LDS read offsets (elements) of this lane's MFMA operands within a stage
+  const int krow = key_perm32(n), kswz = n & 15;  // swz_k32(pi(n)) == n & 15
+  const int vswz = swz_v32(n);                     // swz_v32(32*dt + n) == swz_v32(n)
 
   const int s_begin = R.klo / KS, s_end = (R.khi + KS - 1) / KS, nst = s_end - s_begin;
   const DmaOffsets doff = dma_offsets(P.bs);
-  // prologue: stages 0 .. NSTAGE-2 in flight
+
+  // Keys at or past khi in the last stage may hold stale bits: zero their V so they cannot
+  // reach O.  Called once that stage has landed for every wave.
+  auto zero_tail = [&](u16 *Vl, int k0) {
+    for (int idx = tid; idx < D * KS; idx += NT) {
+      const int d = idx / KS, key = idx % KS;
+      if (k0 + key >= R.khi) Vl[d * KS + 8 * ((key >> 3) ^ swz_v32(d)) + (key & 7)] = 0;
+    }
+    __syncthreads();
+  };
+  // S^T = K . Q^T of one stage
+  auto scores = [&](const u16 *Kl, f32x16 &out) {
+    bf16x8 kf[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+      kf[st] = as_bf16x8(*reinterpret_cast<const uint4 *>(Kl + krow * D + 8 * ((2 * st + g) ^ kswz)));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) out[j] = 0.f;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) out = mfma32_bf16(kf[st], qf[st], out);
+  };
+
+  f32x16 sc;  // scores of the current stage
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i)
     if (i < nst) issue_stage<BSC>(P, R, bt, L, (s_begin + i) * KS, doff, S.st[i], S.vs[i]);
-
+  // The Q loads were issued before these stages: wait for them explicitly (vector loads
+  // complete in order), so the compiler knows Q has landed wherever the loop uses it and
+  // puts no wait for all loads before the score products.
+  wait_dma(4 * min(NSTAGE - 1, nst));
   for (int base = 0; base < nst; base += NSTAGE) {
 #pragma unroll
     for (int u = 0; u < NSTAGE; ++u) {   // unrolled so every stage buffer is a fixed array
       const int i = base + u;
       if (i >= nst) break;
       const int k0 = (s_begin + i) * KS;
-      u16 *buf = S.st[u];
       wait_dma(4 * min(NSTAGE - 2, nst - 1 - i));  // this wave's loads of stage i landed
       stage_barrier();                              // ... and every other wave's
       if (i + NSTAGE - 1 < nst)                     // refill the buffer stage i-1 used
         issue_stage<BSC>(P, R, bt, L, (s_begin + i + NSTAGE - 1) * KS, doff,
                          S.st[(u + NSTAGE - 1) % NSTAGE], S.vs[(u + NSTAGE - 1) % NSTAGE]);
-      if (k0 + KS > R.khi) {
-        // keys at or past khi may hold stale bits: zero their V so they cannot reach O
-        u16 *Vl = S.vs[u];
-        for (int idx = tid; idx < D * KS; idx += NT) {
-          const int d = idx / KS, key = idx % KS;
-          if (k0 + key >= R.khi) Vl[d * KS + 8 * ((key >> 3) ^ swz_v32(d)) + (key & 7)] = 0;
+      if (k0 + KS > R.khi) zero_tail(S.vs[u], k0);
+      // a wave with no rows, or whose rows see none of these keys, has nothing to add
+      if (active && k0 <= wave_hi) {
+        scores(S.st[u], sc);
+        const u16 *Vl = S.vs[u];
+        // V^T operands: feature 32*dt + n, keys 16*h + 8*g .. +7
+        bf16x8 vf[D / 32][2];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            vf[dt][h] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                Vl + (32 * dt + n) * KS + 8 * ((2 * h + g) ^ vswz)));
+        const bool need_mask = (k0 + KS > R.khi) || (k0 + KS - 1 > wave_lo);
+        bf16x8 pf[2];
+        online_softmax_t32(sc, need_mask, k0 + 8 * g, lim, R.khi, P.sl2, m_run, l_run, acc, pf);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          acc[dt] = mfma32_bf16(vf[dt][0], pf[0], acc[dt]);
+          acc[dt] = mfma32_bf16(vf[dt][1], pf[1], acc[dt]);
         }
-        __syncthreads();
-      }
-      if (nrt == 0) continue;
-      const u16 *Kl = buf;
-      const u16 *Vl = S.vs[u];
-      // ---- S^T = K . Q^T for both row tiles, sharing the K operand -------------------
-      bf16x8 kf[2][D / 32];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int keyl = 8 * (r >> 2) + 4 * a + (r & 3);
-        const int sw = swz_k32(keyl);
-#pragma unroll
-        for (int dc = 0; dc < D / 32; ++dc)
-          kf[a][dc] = as_bf16x8(*reinterpret_cast<const uint4 *>(Kl + keyl * D + 8 * ((4 * dc + g) ^ sw)));
-      }
-      f32x4 st0[2][2], st1[2][2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        st0[0][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st1[0][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st0[1][a] = st1[1][a] = f32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};  // 2nd half: none
-#pragma unroll
-        for (int dc = 0; dc < D / 32; ++dc) st0[0][a] = mfma_bf16(kf[a][dc], qf[0][dc], st0[0][a]);
-      }
-      if (nrt > 1) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int dc = 0; dc < D / 32; ++dc) st1[0][a] = mfma_bf16(kf[a][dc], qf[1][dc], st1[0][a]);
-      }
-      // V^T operands of this stage (8 consecutive keys of one feature per lane)
-      bf16x8 vf[D / 16];
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const int d = 16 * dt + r;
-        vf[dt] = as_bf16x8(*reinterpret_cast<const uint4 *>(Vl + d * KS + 8 * (g ^ swz_v32(d))));
-      }
-      const bool need_mask = (k0 + KS > R.khi) || (k0 + KS - 1 > c + R.tok0);
-      bf16x8 pf0[2], pf1[2];
-      online_softmax32(st0[0], need_mask, k0 + 8 * g, lim[0], R.khi, P.sl2, m_run[0], l_run[0],
-                       acc[0], pf0[0]);
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) acc[0][dt] = mfma_bf16(vf[dt], pf0[0], acc[0][dt]);
-      if (nrt > 1) {
-        online_softmax32(st1[0], need_mask, k0 + 8 * g, lim[1], R.khi, P.sl2, m_run[1],
-                         l_run[1], acc[1], pf1[0]);
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) acc[1][dt] = mfma_bf16(vf[dt], pf1[0], acc[1][dt]);
       }
     }
   }
 
   // ---- epilogue: normalise and store, or write the split partial ------------------------
+  if (!active) return;
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (row >= rows) return;
+  // element j of acc[dt] is feature 32*dt + 8*(j/4) + 4*g + j%4 of this lane's row
+  if (R.group < 0) {
+    const int t = qs + tok;
+    if (t >= P.num_tokens) return;
+    const int head = R.h * P.G + row % P.G;
+    const float inv = 1.f / l_run;
+    u16 *op = P.out + ((size_t)t * P.Hq + head) * D + 4 * g;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    if (rt >= nrt) break;
-    float l = l_run[rt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const int row = 32 * w + 16 * rt + r;
-    if (row >= rows) continue;
-    if (R.group < 0) {
-      const int t = qs + R.tok0 + row / P.G;
-      const int head = R.h * P.G + row % P.G;
-      if (t >= P.num_tokens) continue;
-      const float inv = 1.f / l;
-      u16 *op = P.out + ((size_t)t * P.Hq + head) * D + 4 * g;
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const f32x4 a = acc[rt][dt] * inv;
+      for (int q4 = 0; q4 < 4; ++q4) {
         bf16x4 v;
-        v[0] = (__bf16)a[0];
-        v[1] = (__bf16)a[1];
-        v[2] = (__bf16)a[2];
-        v[3] = (__bf16)a[3];
-        *reinterpret_cast<bf16x4 *>(op + 16 * dt) = v;
-      }
-    } else {
-      float *sp = P.ws + R.poff + (int64_t)R.split * slot_floats(MODE_TILE, D);
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        *reinterpret_cast<f32x4 *>(sp + row * D + 16 * dt + 4 * g) = acc[rt][dt];
-      if (g == 0) {
-        sp[TILE_ROWS * D + row] = m_run[rt];
-        sp[TILE_ROWS * D + TILE_ROWS + row] = l;
+        for (int j = 0; j < 4; ++j) v[j] = (__bf16)(acc[dt][4 * q4 + j] * inv);
+        *reinterpret_cast<bf16x4 *>(op + 32 * dt + 8 * q4) = v;
       }
+  } else {
+    float *sp = P.ws + R.poff + (int64_t)R.split * slot_floats(MODE_TILE, D);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4 *>(sp + row * D + 32 * dt + 8 * q4 + 4 * g) =
+            f32x4{acc[dt][4 * q4], acc[dt][4 * q4 + 1], acc[dt][4 * q4 + 2], acc[dt][4 * q4 + 3]};
+    if (g == 0) {
+      sp[TILE_ROWS * D + row] = m_run;
+      sp[TILE_ROWS * D + TILE_ROWS + row] = l_run;
     }
   }
 }
