@@ -340,7 +340,9 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
   double total = 0;
   for (auto &it : base) total += (double)it.cost * Hkv;
   // aim for about two records per compute unit: one full wave of resident workgroups; finer
-  // splits cost partial-result traffic and merge work
+  // splits cost partial-result traffic and merge work.  A shape is cut into round(cost /
+  // target) pieces (not the ceiling): equal shapes slightly above a multiple of the target
+  // would otherwise spill a few records into a second, nearly empty wave.
   const double target = total / (2.0 * num_cus);
   const int32_t min_tiles = 4;  // a split covers at least 4 key tiles (256 keys)
 
@@ -351,7 +353,7 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
   for (auto &it : base) {
     const int32_t tiles = (it.khi + KEY_TILE - 1) / KEY_TILE;
     int32_t nsplit = 1;
-    if (target > 0 && it.cost > target) nsplit = (int32_t)std::ceil(it.cost / target);
+    if (target > 0 && it.cost > target) nsplit = (int32_t)std::lround(it.cost / target);
     nsplit = std::max(1, std::min(nsplit, tiles / min_tiles));
     if (nsplit == 1) {
       items.push_back(it);
