@@ -379,19 +379,48 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
       items.push_back(p);
     }
   }
-  // Longest first (ties keep their order), so the long-running records start early; and the
-  // two kinds interleaved in proportion, so the workgroups resident on a CU mix MFMA-bound
-  // tile records with HBM-bound stream records instead of queueing all of one kind first.
+  // Longest first (ties keep their order), so the long-running records start early.
   std::vector<std::pair<float, int32_t>> &order = cache->plan_order;
   order.resize(items.size());
   for (size_t i = 0; i < items.size(); ++i) order[i] = {-items[i].cost, (int32_t)i};
   std::sort(order.begin(), order.end());
 
+  // Placement across the chip's XCDs (accelerator dies, each with its own L2).  Workgroup i of
+  // a launch runs on XCD i % NUM_XCD, in launch order within the XCD.  A record of sequence s,
+  // KV head h and query tile t goes to XCD (h + Hkv*(s + t)) % NUM_XCD.  With Hkv a multiple
+  // of NUM_XCD that is h % NUM_XCD: all tile records of one (sequence, head) read the same
+  // keys on one XCD, so their K/V comes from HBM once and from that XCD's L2 for the others,
+  // and every XCD gets the same share of each item.  With fewer heads the query tiles rotate
+  // over the XCDs instead, so that a single sequence still uses the whole chip.
+  // Within an XCD the records keep the longest-first order, and the two kinds are interleaved
+  // in proportion so that the workgroups resident on a CU mix MFMA-bound tile records with
+  // HBM-bound stream records.  XCD lists that run short are padded with null records
+  // (sequence -1) that exit at once.
+  constexpr int NUM_XCD = 8;
+  std::vector<int32_t> *lists = cache->plan_lists;  // per XCD: item * Hkv + head
+  int64_t xcd_tiles[NUM_XCD] = {0};
+  for (int k = 0; k < NUM_XCD; ++k) lists[k].clear();
+  if ((int64_t)items.size() * Hkv > INT32_MAX) return fail(FG_E_UNSUPPORTED, "too many records");
+  for (int pass = 0; pass < 2; ++pass)  // tile records first, then stream records
+    for (const auto &o : order) {
+      const PlanItem &p = items[o.second];
+      if ((p.mode == MODE_TILE) != (pass == 0)) continue;
+      const int64_t tile = p.mode == MODE_TILE ? p.tok0 / (TILE_ROWS / G) : 0;
+      const int32_t rot = (int32_t)(((int64_t)Hkv * (p.s + tile)) % NUM_XCD);
+      for (int32_t h = 0; h < Hkv; ++h) {
+        const int x = (h + rot) % NUM_XCD;
+        lists[x].push_back(o.second * Hkv + h);
+        if (pass == 0) ++xcd_tiles[x];
+      }
+    }
+  size_t longest = 0;
+  for (int k = 0; k < NUM_XCD; ++k) longest = std::max(longest, lists[k].size());
+  const int64_t n_slots = (int64_t)longest * NUM_XCD;  // main records including padding
+
   const int64_t ws = groups ? poff_bytes : 0;
   if ((ws / 4) > INT32_MAX) return fail(FG_E_UNSUPPORTED, "workspace beyond 8 GiB");
-  const int64_t n_main = (int64_t)items.size() * Hkv;
-  if (n_main + groups > INT32_MAX) return fail(FG_E_UNSUPPORTED, "too many records");
-  info->num_work = (int32_t)(n_main + groups);
+  if (n_slots + groups > INT32_MAX) return fail(FG_E_UNSUPPORTED, "too many records");
+  info->num_work = (int32_t)(n_slots + groups);
   info->num_groups = groups;
   info->workspace_bytes = ws;
   if (work_capacity < info->num_work) {
@@ -399,27 +428,27 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
     return fail(FG_E_ARG, "work capacity %d < %d records", work_capacity, info->num_work);
   }
   if (info->num_work > 0 && !work) return fail(FG_E_ARG, "work is null");
-  // Each item expands to one record per KV head. Records of the two kinds are interleaved in
-  // proportion (Bresenham-style), each kind keeping its longest-first order.
-  std::vector<int32_t> &kinds = cache->plan_kinds;  // tile items, then stream items, in order
-  kinds.clear();
-  for (int pass = 0; pass < 2; ++pass)
-    for (const auto &o : order)
-      if ((items[o.second].mode == MODE_TILE) == (pass == 0)) kinds.push_back(o.second);
-  size_t n_tile_items = 0;
-  while (n_tile_items < kinds.size() && items[kinds[n_tile_items]].mode == MODE_TILE) ++n_tile_items;
-  const int64_t nt = (int64_t)n_tile_items * Hkv, ns = (int64_t)(kinds.size() - n_tile_items) * Hkv;
-  int32_t *w = work;
-  int32_t *merge = work + n_main * FG_WORK_INTS;  // merge record of group g at merge[g]
-  int64_t it = 0, is = 0, err = 0;
-  for (int64_t k = 0; k < nt + ns; ++k, w += FG_WORK_INTS) {
-    const bool take_tile = is == ns || (it < nt && err <= 0);
-    err += take_tile ? ns : -nt;
-    const int64_t r = take_tile ? it++ : is++;  // record index within its kind
-    const PlanItem &p = items[kinds[(take_tile ? 0 : n_tile_items) + r / Hkv]];
-    const int32_t h = (int32_t)(r % Hkv);
-    const int64_t group_bytes = (int64_t)p.nsplit * slot_floats(p.mode, D) * 4;
-    {
+
+  int32_t *merge = work + n_slots * FG_WORK_INTS;  // merge record of group g at merge[g]
+  for (int k = 0; k < NUM_XCD; ++k) {
+    const std::vector<int32_t> &lst = lists[k];
+    const int64_t nt = xcd_tiles[k], ns = (int64_t)lst.size() - nt;
+    int64_t it = 0, is = 0, err = 0;
+    for (int64_t j = 0; j < (int64_t)longest; ++j) {
+      int32_t *w = work + (j * NUM_XCD + k) * FG_WORK_INTS;
+      if (j >= (int64_t)lst.size()) {  // padding
+        for (int f = 0; f < FG_WORK_INTS; ++f) w[f] = 0;
+        w[W_SEQ] = -1;
+        w[W_GROUP] = -1;
+        continue;
+      }
+      // tile and stream records in proportion (Bresenham-style), each in its list order
+      const bool take_tile = is == ns || (it < nt && err <= 0);
+      err += take_tile ? ns : -nt;
+      const int32_t code = lst[take_tile ? it++ : nt + is++];
+      const PlanItem &p = items[code / Hkv];
+      const int32_t h = code % Hkv;
+      const int64_t group_bytes = (int64_t)p.nsplit * slot_floats(p.mode, D) * 4;
       const int32_t g = p.group >= 0 ? p.group + h : -1;
       const int32_t poff = p.group >= 0 ? (int32_t)((p.poff + h * group_bytes) / 4) : 0;
       w[W_SEQ] = p.s;

@@ -25,7 +25,7 @@ struct fg_cache {
   // planner scratch, reused across calls so planning allocates nothing in steady state
   mutable std::vector<fgi::PlanItem> plan_base, plan_items;
   mutable std::vector<std::pair<float, int32_t>> plan_order;
-  mutable std::vector<int32_t> plan_kinds;
+  mutable std::vector<int32_t> plan_lists[8];  // per XCD record lists
 };
 
 namespace fgi {

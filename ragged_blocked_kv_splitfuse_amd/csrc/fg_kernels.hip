@@ -381,9 +381,8 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
   // ---- merge the four waves through LDS ------------------------------------------------
   // per-wave O^T dumps: wave w uses the K half of stage buffer w (8 KiB = 16 rows x 128);
   // a select chain keeps every LDS address tied to a fixed array
-  float *so_w = reinterpret_cast<float *>(w == 0 ? S.st[0] : w == 1 ? S.st[1]
-                                          : w == 2 ? S.st[2] : S.st[3]);
-  float *sm = reinterpret_cast<float *>(S.vs[0]);              // [NW][16]
+  float *so_w = reinterpret_cast<float *>(S.k(w));
+  float *sm = reinterpret_cast<float *>(S.v(0));               // [NW][16]
   float *sl = sm + NW * STREAM_ROWS;                           // [NW][16]
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
@@ -404,7 +403,7 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
     const float m = sm[ww * STREAM_ROWS + row];
     const float f = (m == NEG_INF) ? 0.f : fast_exp2(m - M);
     Lsum += sl[ww * STREAM_ROWS + row] * f;
-    const float *src = reinterpret_cast<const float *>(S.st[ww]) + row * D + chunk * 8;
+    const float *src = reinterpret_cast<const float *>(S.k(ww)) + row * D + chunk * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] += src[i] * f;
   }
@@ -441,7 +440,7 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
 constexpr int KS = 32;                     // keys per stage
 constexpr int NSTAGE = 4;                  // ring depth
 constexpr int STAGE_K = KS * D;            // u16 elements of the K part of a stage
-constexpr int STAGE_ELEMS = 2 * KS * D;    // K + V^T: 16 KiB (two 8 KiB arrays)
+constexpr int STAGE_ELEMS = 2 * KS * D;    // K + V^T: 16 KiB
 static_assert(STREAM_ROWS * D * 4 <= STAGE_K * 2, "a wave's stream dump must fit a K array");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -460,13 +459,34 @@ __device__ __forceinline__ int key_perm32(int m) {
   return (m & ~12) | ((m >> 1) & 4) | ((m << 1) & 8);
 }
 
+// The stage ring: one workgroup-shared array, stage buffer i = K [32 keys][128] followed by
+// V^T [128][32 keys].  Buffers are addressed as base + constant offset, so one set of per-lane
+// address registers serves every buffer.
+constexpr int MAX_IDS = 256;  // block ids of a tile record staged in LDS
+
 struct Lds {
-  u16 *st[NSTAGE];
-  u16 *vs[NSTAGE];
+  u16 *base;
+  int *ids;  // MAX_IDS block ids
+  __device__ u16 *k(int i) const { return base + i * STAGE_ELEMS; }
+  __device__ u16 *v(int i) const { return base + i * STAGE_ELEMS + STAGE_K; }
 };
 
-__device__ __forceinline__ void dma16(const u16 *src, u16 *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)lds_wave_base, 16, 0, 0);
+// One wave instruction: 16 bytes per lane from global memory to LDS at lds_wave_base + 16*lane.
+// Written as inline asm (M0 holds the wave's LDS base) so that the compiler does not track
+// these loads: its alias tracking of LDS-DMA targets is easily lost and then drains every
+// prefetched stage before ordinary LDS reads.  The kernel waits for the loads itself
+// (wait_dma) and separates them from LDS reads by barriers; the "memory" clobber keeps the
+// compiler from moving memory operations across them.  Nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16(const u16 *src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "memory");
+}
+
+// LDS byte address of a workgroup-shared array (a constant once the array is known)
+__device__ __forceinline__ uint32_t lds_addr_of(const u16 *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const u16 *)p;
 }
 
 // Workgroup barrier for the stage ring.  __syncthreads() would also drain every vector load
@@ -512,25 +532,25 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int bs) {
   return o;
 }
 
+// blk: the stage's block id, read ahead by the caller (used when a stage lies in one block)
 template <int BSC>
 __device__ __forceinline__ void issue_stage(const Params &P, const Rec &R, const int32_t *bt,
-                                            int L, int k0, const DmaOffsets &o, u16 *buf,
-                                            u16 *vbuf) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+                                            int L, int k0, int blk, const DmaOffsets &o,
+                                            u16 *buf, u16 *vbuf) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int bs_mask = P.bs - 1;
   const size_t head_stride = (size_t)P.bs * D;
+  const uint32_t kl = lds_addr_of(buf) + 2048u * w, vl = lds_addr_of(vbuf) + 2048u * w;
   if (BSC >= 1) {
     // a 32-key stage lies in one block: uniform base + per-lane offset
-    const int blk = clamp_block(ldc(bt, k0 >> P.bs_log2), P.num_blocks);
     const size_t hb = ((size_t)blk * P.Hkv + R.h) * head_stride;
     const char *kb = reinterpret_cast<const char *>(P.k_pool + hb + (size_t)(k0 & bs_mask) * D);
     const char *vb = reinterpret_cast<const char *>(P.v_pool + hb + (k0 & bs_mask));
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      dma16(reinterpret_cast<const u16 *>(kb + o.k[p]), buf + (2 * w + p) * 512);
+    for (int p = 0; p < 2; ++p) dma16(reinterpret_cast<const u16 *>(kb + o.k[p]), kl + 1024u * p);
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      dma16(reinterpret_cast<const u16 *>(vb + o.v[p]), vbuf + (2 * w + p) * 512);
+    for (int p = 0; p < 2; ++p) dma16(reinterpret_cast<const u16 *>(vb + o.v[p]), vl + 1024u * p);
     return;
   }
 #pragma unroll
@@ -540,7 +560,7 @@ __device__ __forceinline__ void issue_stage(const Params &P, const Rec &R, const
     const int key = min(k0 + keyl, L - 1);
     const int blk = clamp_block(bt[key >> P.bs_log2], P.num_blocks);
     dma16(P.k_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)(key & bs_mask) * D + 8 * ch,
-          buf + reg * 512);
+          kl + 1024u * p);
   }
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
@@ -549,23 +569,23 @@ __device__ __forceinline__ void issue_stage(const Params &P, const Rec &R, const
     const int key0 = min(k0 + 8 * kc, (L - 1) & ~7);
     const int blk = clamp_block(bt[key0 >> P.bs_log2], P.num_blocks);
     dma16(P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)d * P.bs + (key0 & bs_mask),
-          vbuf + reg * 512);
+          vl + 1024u * p);
   }
 }
 
 // Online softmax over one 32-key stage for this lane's query row: s[j] is the raw score of key
 // key0 + 16*(j/8) + j%8 (key0 = k0 + 8*(l/32)).  Same arithmetic as online_softmax; P comes
 // back as the two B operands of the P.V product.
-__device__ __forceinline__ void online_softmax_t32(f32x16 &s, bool need_mask, int key0, int lim,
-                                                   int khi, float sl2, float &m, float &l,
-                                                   f32x16 *acc, bf16x8 (&pf)[2]) {
-  if (need_mask) {
+__device__ __forceinline__ void mask_t32(f32x16 &s, int key0, int lim, int khi) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = key0 + 16 * (j / 8) + j % 8;
-      if (key > lim || key >= khi) s[j] = NEG_INF;
-    }
+  for (int j = 0; j < 16; ++j) {
+    const int key = key0 + 16 * (j / 8) + j % 8;
+    if (key > lim || key >= khi) s[j] = NEG_INF;
   }
+}
+
+__device__ __forceinline__ void online_softmax_t32(f32x16 &s, float sl2, float &m, float &l,
+                                                   f32x16 *acc, bf16x8 (&pf)[2]) {
   float mx = s[0];
 #pragma unroll
   for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
@@ -590,6 +610,30 @@ __device__ __forceinline__ void online_softmax_t32(f32x16 &s, bool need_mask, in
   pf[1] = to_bf16x8(p + 8);
 }
 
+// The common case of a stage, in place: exponentials against the current running max m.  While
+// every p stays within 2^LAZY_TAU -- which their sum bounds -- that max may stand, and the stage
+// needs no max reduction and no rescale.  Returns false when it may not (a new max more than
+// LAZY_TAU above m, the first stage with m = -inf giving an inf or NaN sum, an overflow); then
+// s holds no scores any more and the caller redoes the stage with online_softmax_t32.
+__device__ __forceinline__ bool softmax_t32_fast(f32x16 &s, float sl2, float m, float &l,
+                                                 bf16x8 (&pf)[2]) {
+  constexpr float P_CAP = 256.f;  // 2^LAZY_TAU
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    s[j] = fast_exp2(fmaf(s[j], sl2, -m));
+    psum += s[j];
+  }
+  if (__ballot(!(psum <= P_CAP))) return false;
+  l += psum;
+  float p[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) p[j] = s[j];
+  pf[0] = to_bf16x8(p);
+  pf[1] = to_bf16x8(p + 8);
+  return true;
+}
+
 template <int BSC>
 __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
@@ -606,19 +650,6 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
   const int row = 32 * w + n;
   const int tok = R.tok0 + row / P.G;
   const int lim = c + tok;  // keys 0 .. lim are visible to this lane's row
-  bf16x8 qf[D / 16];
-  {
-    const int t = qs + tok, head = R.h * P.G + row % P.G;
-    const bool ok = row < rows && t < P.num_tokens;
-    // rows past the record read token 0 (always present) and are zeroed: unconditional loads
-    // let the compiler see that the wait after the prologue covers them
-    const u16 *qp = P.q + ((size_t)(ok ? t : 0) * P.Hq + (ok ? head : 0)) * D + 8 * g;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      const uint4 v = ld16(qp + 16 * st);
-      qf[st] = as_bf16x8(ok ? v : make_uint4(0, 0, 0, 0));
-    }
-  }
   float m_run = NEG_INF, l_run = 0.f;
   f32x16 acc[D / 32];
 #pragma unroll
@@ -642,6 +673,7 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
     }
     __syncthreads();
   };
+  bf16x8 qf[D / 16];  // B operands of the score product (loaded after the prologue below)
   // S^T = K . Q^T of one stage
   auto scores = [&](const u16 *Kl, f32x16 &out) {
     bf16x8 kf[D / 16];
@@ -655,13 +687,46 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
   };
 
   f32x16 sc;  // scores of the current stage
+  // block id of a stage (scalar load; stages of a block-size >= 32 cache lie in one block)
+  // When the record's blocks fit, their ids are staged in LDS first: an LDS read of the next
+  // id is cheap, while a scalar load's latency would surface at the next LDS wait (scalar and
+  // LDS reads share one counter).
+  const int b_first = R.klo >> P.bs_log2;
+  const int n_ids = BSC >= 1 ? ((R.khi - 1) >> P.bs_log2) - b_first + 1 : 0;
+  const bool ids_in_lds = n_ids <= MAX_IDS;
+  if (BSC >= 1 && ids_in_lds) {
+    for (int i = tid; i < n_ids; i += NT) S.ids[i] = clamp_block(bt[b_first + i], P.num_blocks);
+    __syncthreads();
+  }
+  // (the LDS read lands in a vector register; it is made scalar only where it is used, one
+  // stage later, so no wait for it stalls the loop)
+  auto stage_block = [&](int i) {
+    if (BSC == 0) return 0;
+    const int b = ((s_begin + i) * KS) >> P.bs_log2;
+    return ids_in_lds ? S.ids[b - b_first] : clamp_block(ldc(bt, b), P.num_blocks);
+  };
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i)
-    if (i < nst) issue_stage<BSC>(P, R, bt, L, (s_begin + i) * KS, doff, S.st[i], S.vs[i]);
-  // The Q loads were issued before these stages: wait for them explicitly (vector loads
-  // complete in order), so the compiler knows Q has landed wherever the loop uses it and
-  // puts no wait for all loads before the score products.
-  wait_dma(4 * min(NSTAGE - 1, nst));
+    if (i < nst)
+      issue_stage<BSC>(P, R, bt, L, (s_begin + i) * KS,
+                       __builtin_amdgcn_readfirstlane(stage_block(i)), doff, S.k(i), S.v(i));
+  // the block id of the next stage to fetch is read one stage ahead, so that the scalar
+  // load's latency never stalls the loop
+  int blk_next = NSTAGE - 1 < nst ? stage_block(NSTAGE - 1) : 0;
+  // Q is loaded after the prologue stages; the compiler waits for it (and, loads completing
+  // in order, for those stages) before its first use.
+  {
+    const int t = qs + tok, head = R.h * P.G + row % P.G;
+    const bool ok = row < rows && t < P.num_tokens;
+    // rows past the record read token 0 (always present) and are zeroed
+    const u16 *qp = P.q + ((size_t)(ok ? t : 0) * P.Hq + (ok ? head : 0)) * D + 8 * g;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const uint4 v = ld16(qp + 16 * st);
+      qf[st] = as_bf16x8(ok ? v : make_uint4(0, 0, 0, 0));
+    }
+  }
+
   for (int base = 0; base < nst; base += NSTAGE) {
 #pragma unroll
     for (int u = 0; u < NSTAGE; ++u) {   // unrolled so every stage buffer is a fixed array
@@ -670,14 +735,17 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
       const int k0 = (s_begin + i) * KS;
       wait_dma(4 * min(NSTAGE - 2, nst - 1 - i));  // this wave's loads of stage i landed
       stage_barrier();                              // ... and every other wave's
-      if (i + NSTAGE - 1 < nst)                     // refill the buffer stage i-1 used
-        issue_stage<BSC>(P, R, bt, L, (s_begin + i + NSTAGE - 1) * KS, doff,
-                         S.st[(u + NSTAGE - 1) % NSTAGE], S.vs[(u + NSTAGE - 1) % NSTAGE]);
-      if (k0 + KS > R.khi) zero_tail(S.vs[u], k0);
+      if (i + NSTAGE - 1 < nst) {                   // refill the buffer stage i-1 used
+        issue_stage<BSC>(P, R, bt, L, (s_begin + i + NSTAGE - 1) * KS,
+                         __builtin_amdgcn_readfirstlane(blk_next), doff,
+                         S.k((u + NSTAGE - 1) % NSTAGE), S.v((u + NSTAGE - 1) % NSTAGE));
+        if (i + NSTAGE < nst) blk_next = stage_block(i + NSTAGE);
+      }
+      if (k0 + KS > R.khi) zero_tail(S.v(u), k0);
       // a wave with no rows, or whose rows see none of these keys, has nothing to add
       if (active && k0 <= wave_hi) {
-        scores(S.st[u], sc);
-        const u16 *Vl = S.vs[u];
+        scores(S.k(u), sc);
+        const u16 *Vl = S.v(u);
         // V^T operands: feature 32*dt + n, keys 16*h + 8*g .. +7
         bf16x8 vf[D / 32][2];
 #pragma unroll
@@ -687,8 +755,14 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
             vf[dt][h] = as_bf16x8(*reinterpret_cast<const uint4 *>(
                 Vl + (32 * dt + n) * KS + 8 * ((2 * h + g) ^ vswz)));
         const bool need_mask = (k0 + KS > R.khi) || (k0 + KS - 1 > wave_lo);
+        if (need_mask) mask_t32(sc, k0 + 8 * g, lim, R.khi);
         bf16x8 pf[2];
-        online_softmax_t32(sc, need_mask, k0 + 8 * g, lim, R.khi, P.sl2, m_run, l_run, acc, pf);
+        if (!softmax_t32_fast(sc, P.sl2, m_run, l_run, pf)) {
+          // rare: recompute the scores (the stage is still in LDS) and take the full path
+          scores(S.k(u), sc);
+          if (need_mask) mask_t32(sc, k0 + 8 * g, lim, R.khi);
+          online_softmax_t32(sc, P.sl2, m_run, l_run, acc, pf);
+        }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           acc[dt] = mfma32_bf16(vf[dt][0], pf[0], acc[dt]);
@@ -738,25 +812,13 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
 // BSC: 0 = blocks of < 32 keys, 1 = blocks of 32 keys, 2 = blocks of >= 64 keys.
 template <int BSC>
 __global__ __launch_bounds__(NT, 2) void attention_bf16_kernel(Params P) {
-  __shared__ __attribute__((aligned(16))) u16 st0[STAGE_ELEMS / 2];
-  __shared__ __attribute__((aligned(16))) u16 st1[STAGE_ELEMS / 2];
-  __shared__ __attribute__((aligned(16))) u16 st2[STAGE_ELEMS / 2];
-  __shared__ __attribute__((aligned(16))) u16 st3[STAGE_ELEMS / 2];
-  __shared__ __attribute__((aligned(16))) u16 vs0[STAGE_ELEMS / 2];
-  __shared__ __attribute__((aligned(16))) u16 vs1[STAGE_ELEMS / 2];
-  __shared__ __attribute__((aligned(16))) u16 vs2[STAGE_ELEMS / 2];
-  __shared__ __attribute__((aligned(16))) u16 vs3[STAGE_ELEMS / 2];
+  __shared__ __attribute__((aligned(16))) u16 ring[NSTAGE * STAGE_ELEMS];
+  __shared__ int blk_ids[MAX_IDS];
   const Rec R = load_rec(P.work + (size_t)blockIdx.x * FG_WORK_INTS);
   if (R.s < 0 || !rec_fits_workspace(P, R)) return;  // never write outside the workspace
   Lds S;
-  S.st[0] = st0;
-  S.st[1] = st1;
-  S.st[2] = st2;
-  S.st[3] = st3;
-  S.vs[0] = vs0;
-  S.vs[1] = vs1;
-  S.vs[2] = vs2;
-  S.vs[3] = vs3;
+  S.base = ring;
+  S.ids = blk_ids;
   if (R.mode == MODE_STREAM)
     stream_record<BSC == 2>(P, R, S);
   else

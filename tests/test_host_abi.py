@@ -292,7 +292,21 @@ def check_plan(hb, info, work, hq, hkv, head_dim=128):
     slot = {0: 16 * (head_dim + 2), 1: 128 * (head_dim + 2)}
     groups = {}
     cover = {}
+    # the main list is laid out for the 8 XCDs (record i runs on XCD i % 8); lists that run
+    # short are padded with null records at their end
+    assert len(main) % 8 == 0
+    xcd_of_tile_group = {}
+    for i, rec in enumerate(main):
+        if int(rec[0]) == -1:
+            assert int(rec[7]) == -1
+            assert all(int(r[0]) == -1 for r in main[i::8]), "padding only at an XCD list's end"
+            continue
+        s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff, _ = (int(x) for x in rec)
+        if mode == 1 and hkv % 8 == 0:  # tile records of one (sequence, head) share an XCD
+            assert xcd_of_tile_group.setdefault((s, h), i % 8) == i % 8
     for rec in main:
+        if int(rec[0]) == -1:
+            continue
         s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff, _ = (int(x) for x in rec)
         assert 0 <= s < S and 0 <= h < hkv and nt >= 1 and sp >= 0
         assert mode == (0 if nt * G <= 16 else 1) and nt * G <= 128
