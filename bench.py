@@ -109,24 +109,35 @@ def main():
     sh = stream_handle(stream)
     kptr, vptr = cache.k_pool.data_ptr(), cache.v_pool.data_ptr()
 
-    work_buf = np.zeros((1 << 16, fg.FG_WORK_INTS), np.int32)
+    work_buf = np.zeros(1 << 20, np.int32)
+
+    # One cache handle for the run.  Every step starts from the same state: the sequence
+    # states are copied back, and the blocks the step's composition took are returned in
+    # reverse order, which restores the free list exactly (it is a stack, handed out from the
+    # front of free_ids).
+    h = fg.fg_blocked_cache_init(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                                 w.dtype, kptr, vptr, free_ids)
+    n_free0 = fg.fg_blocked_cache_num_free(h)
 
     def compose_and_plan():
         ctypes.memmove(ctypes.addressof(ss.arr), arr_bytes, len(arr_bytes))
         np.copyto(ss.blocks, blocks0)
-        h = fg.fg_blocked_cache_init(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
-                                     w.dtype, kptr, vptr, free_ids)
         st = fg.fg_splitfuse_compose(h, ss, w.budget, hb)
         assert st == fg.FG_OK
         info, work = fg.fg_attention_plan(h, hb, w.num_q_heads, S["cus"], work_buf)
         return h, info, work
+
+    def restore_free_list():
+        taken = n_free0 - fg.fg_blocked_cache_num_free(h)
+        if taken:
+            fg.fg_blocked_cache_release(h, free_ids[taken - 1::-1])
 
     # pass shape and inputs
     h, info, work = compose_and_plan()
     T, nseq = hb.num_tokens, hb.num_seqs
     ctx = hb.context_len[:nseq].astype(np.int64)
     nq = hb.n_query[:nseq].astype(np.int64)
-    fg.fg_blocked_cache_destroy(h)
+    restore_free_list()
     g = torch.Generator(device="cuda")
     g.manual_seed(w.seed * 104729 + 17)
     mk = lambda heads: (torch.randn((T, heads, w.head_dim), generator=g, device="cuda")
@@ -157,7 +168,7 @@ def main():
         fg.fg_ragged_attention(h, c, info, desc.work_ptr, q.data_ptr(), w.num_q_heads, w.scale,
                                out.data_ptr(), wptr, wbytes, sh)
         ev[i][2].record(stream)
-        fg.fg_blocked_cache_destroy(h)
+        restore_free_list()
         host_s.append(time.perf_counter() - t0)
 
     for i in range(args.warmup):

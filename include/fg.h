@@ -57,8 +57,8 @@ typedef enum fg_status {
 
 typedef enum fg_dtype { FG_F32 = 0, FG_BF16 = 1 } fg_dtype;
 
-/* Number of int32 per work-list record produced by fg_attention_plan. */
-#define FG_WORK_INTS 12
+/* Number of int32 per work item in the work list produced by fg_attention_plan. */
+#define FG_ITEM_INTS 12
 
 typedef struct fg_cache fg_cache; /* opaque, host-side */
 
@@ -100,12 +100,15 @@ typedef struct fg_ragged_batch {
 } fg_ragged_batch;
 
 typedef struct fg_attention_plan_info {
-  int32_t num_work;          /* records in the work list: attention records, then one merge
-                                record per split group (written if capacity allowed) */
+  int32_t num_work;          /* records: attention records (workgroups of the main launch,
+                                padding included), then one merge record per split group */
   int32_t num_groups;        /* key-range split groups = merge records (the last ones) */
   int64_t workspace_bytes;   /* device workspace for split partials (0: none needed) */
   int32_t num_q_heads;       /* Hq the plan was made for */
   int32_t num_tokens;        /* T of the batch the plan was made for */
+  int32_t num_items;         /* work items (query tile x key split, shared by the KV heads) */
+  int32_t work_ints;         /* int32 the work list occupies:
+                                num_items * FG_ITEM_INTS + num_work */
 } fg_attention_plan_info;
 
 /* ---- cache handle and block allocator ------------------------------------------------ */
@@ -162,14 +165,19 @@ fg_status fg_validate_batch(const fg_cache *cache, const fg_ragged_batch *host);
 fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const void *k_new,
                        const void *v_new, void *stream);
 
-/* Splits the attention of a host batch into work records (host only).  Sequences with at
- * most 16 query rows (rows = tokens x query heads per KV head) become key-streaming
- * records, others become tiles of up to 128 rows; long key ranges are split so that about
- * num_cus * 2 records' worth of work exists, and records come longest first.  Each split
- * group also gets a merge record after all attention records.  Writes the num_work records
- * of FG_WORK_INTS int32 into `work` (host) and fills *info; with work_capacity 0 it only
- * sizes (FG_OK), with 0 < work_capacity < num_work it returns FG_E_ARG.  The caller copies
- * `work` to the device. */
+/* Splits the attention of a host batch into work (host only).  Sequences with at most 16
+ * query rows (rows = tokens x query heads per KV head) become key-streaming items, others
+ * tiles of up to 128 rows; long key ranges are split so that about num_cus * 2 records'
+ * worth of work exists.  A record is one item for one KV head.  The work list, info->
+ * work_ints int32 written to `work` (host), is
+ *   items[num_items][FG_ITEM_INTS]   the items (layout private to this library), then
+ *   codes[num_work]                  record r = codes[r]: item * Hkv + KV head, or -1 for a
+ *                                    padding record; the last num_groups are the merge
+ *                                    records of the split groups.
+ * Records come longest first, laid out so that record r runs on XCD r % 8 of the launch
+ * with all records of a (sequence, KV head) on one XCD.  With work_capacity (in int32) 0 it
+ * only sizes (FG_OK); with 0 < work_capacity < work_ints it returns FG_E_ARG.  The caller
+ * copies `work` to the device. */
 fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *host,
                             int32_t num_q_heads, int32_t num_cus,
                             fg_attention_plan_info *info, int32_t *work,
@@ -181,7 +189,7 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *host,
  * on bf16 MFMA with fp32 accumulation, P rounded to bf16 for the P.V product, output
  * rounded to nearest even; fp32 inputs: fp32 arithmetic.  `dev` arrays, q, out, work_dev
  * and workspace are device memory; `plan` is the host info fg_attention_plan returned for
- * this batch and work_dev the device copy of its records (both unused for FG_F32).  One
+ * this batch and work_dev the device copy of its work list (both unused for FG_F32).  One
  * launch runs every attention record (decode and chunk rows together); a second, small
  * launch merges split groups when the plan has any.  The workspace needs no initialisation
  * (its contents are scratch); calls sharing a workspace must be ordered on one stream.

@@ -131,17 +131,18 @@ fg_status fg_blocked_cache_release(fg_cache *cache, const int32_t *blocks, int32
   clear_error();
   if (!cache) return fail(FG_E_ARG, "null cache");
   if (n < 0 || (n > 0 && !blocks)) return fail(FG_E_ARG, "bad block list");
-  std::vector<uint8_t> seen(cache->cfg.num_blocks, 0);
+  // validate and mark in one sweep (O(n), no per-call table); a bad id undoes the marks
   for (int32_t i = 0; i < n; ++i) {
     const int32_t b = blocks[i];
-    if (b < 0 || b >= cache->cfg.num_blocks) return fail(FG_E_ARG, "block %d out of range", b);
-    if (cache->is_free[b] || seen[b]) return fail(FG_E_ARG, "block %d is already free", b);
-    seen[b] = 1;
+    const bool bad = b < 0 || b >= cache->cfg.num_blocks || cache->is_free[b];
+    if (bad) {
+      for (int32_t j = 0; j < i; ++j) cache->is_free[blocks[j]] = 0;
+      if (b < 0 || b >= cache->cfg.num_blocks) return fail(FG_E_ARG, "block %d out of range", b);
+      return fail(FG_E_ARG, "block %d is already free", b);
+    }
+    cache->is_free[b] = 1;
   }
-  for (int32_t i = 0; i < n; ++i) {
-    cache->free_stack.push_back(blocks[i]);
-    cache->is_free[blocks[i]] = 1;
-  }
+  cache->free_stack.insert(cache->free_stack.end(), blocks, blocks + n);
   return FG_OK;
 }
 
@@ -353,7 +354,11 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
   for (auto &it : base) {
     const int32_t tiles = (it.khi + KEY_TILE - 1) / KEY_TILE;
     int32_t nsplit = 1;
-    if (target > 0 && it.cost > target) nsplit = (int32_t)std::lround(it.cost / target);
+    // Stream records are cut 8x finer: one streams at a fixed per-workgroup rate however idle
+    // the chip is, so a long one becomes the pass's tail, while its split partial (16 rows) is
+    // cheap to write and merge.  Tile splits cost a 128-row partial and a Q reload each.
+    const double tg = it.mode == MODE_STREAM ? target / 8 : target;
+    if (tg > 0 && it.cost > tg) nsplit = (int32_t)std::lround(it.cost / tg);
     nsplit = std::max(1, std::min(nsplit, tiles / min_tiles));
     if (nsplit == 1) {
       items.push_back(it);
@@ -419,58 +424,60 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
 
   const int64_t ws = groups ? poff_bytes : 0;
   if ((ws / 4) > INT32_MAX) return fail(FG_E_UNSUPPORTED, "workspace beyond 8 GiB");
-  if (n_slots + groups > INT32_MAX) return fail(FG_E_UNSUPPORTED, "too many records");
+  const int64_t n_items = (int64_t)items.size();
+  const int64_t n_ints = n_items * FG_ITEM_INTS + n_slots + groups;
+  if (n_ints > INT32_MAX) return fail(FG_E_UNSUPPORTED, "too many records");
   info->num_work = (int32_t)(n_slots + groups);
   info->num_groups = groups;
   info->workspace_bytes = ws;
-  if (work_capacity < info->num_work) {
+  info->num_items = (int32_t)n_items;
+  info->work_ints = (int32_t)n_ints;
+  if (work_capacity < info->work_ints) {
     if (work_capacity == 0) return FG_OK;  // sizing call
-    return fail(FG_E_ARG, "work capacity %d < %d records", work_capacity, info->num_work);
+    return fail(FG_E_ARG, "work capacity %d < %d int32", work_capacity, info->work_ints);
   }
-  if (info->num_work > 0 && !work) return fail(FG_E_ARG, "work is null");
+  if (n_ints == 0) return FG_OK;
+  if (!work) return fail(FG_E_ARG, "work is null");
 
-  int32_t *merge = work + n_slots * FG_WORK_INTS;  // merge record of group g at merge[g]
+  // the items
+  for (int64_t i = 0; i < n_items; ++i) {
+    const PlanItem &p = items[i];
+    int32_t *w = work + i * FG_ITEM_INTS;
+    w[I_SEQ] = p.s;
+    w[I_TOK0] = p.tok0;
+    w[I_NTOK] = p.ntok;
+    w[I_KLO] = p.klo;
+    w[I_KHI] = p.khi;
+    w[I_MODE] = p.mode;
+    w[I_GROUP] = p.group;
+    w[I_SPLIT] = p.split;
+    w[I_NSPLIT] = p.nsplit;
+    w[I_POFF] = p.group >= 0 ? (int32_t)(p.poff / 4) : 0;
+    w[I_RES0] = 0;
+    w[I_RES1] = 0;
+  }
+  // the record codes, XCD-interleaved, then the merge records (split 0 of each group)
+  int32_t *codes = work + n_items * FG_ITEM_INTS;
   for (int k = 0; k < NUM_XCD; ++k) {
     const std::vector<int32_t> &lst = lists[k];
     const int64_t nt = xcd_tiles[k], ns = (int64_t)lst.size() - nt;
     int64_t it = 0, is = 0, err = 0;
     for (int64_t j = 0; j < (int64_t)longest; ++j) {
-      int32_t *w = work + (j * NUM_XCD + k) * FG_WORK_INTS;
+      int32_t &code = codes[j * NUM_XCD + k];
       if (j >= (int64_t)lst.size()) {  // padding
-        for (int f = 0; f < FG_WORK_INTS; ++f) w[f] = 0;
-        w[W_SEQ] = -1;
-        w[W_GROUP] = -1;
+        code = -1;
         continue;
       }
       // tile and stream records in proportion (Bresenham-style), each in its list order
       const bool take_tile = is == ns || (it < nt && err <= 0);
       err += take_tile ? ns : -nt;
-      const int32_t code = lst[take_tile ? it++ : nt + is++];
-      const PlanItem &p = items[code / Hkv];
-      const int32_t h = code % Hkv;
-      const int64_t group_bytes = (int64_t)p.nsplit * slot_floats(p.mode, D) * 4;
-      const int32_t g = p.group >= 0 ? p.group + h : -1;
-      const int32_t poff = p.group >= 0 ? (int32_t)((p.poff + h * group_bytes) / 4) : 0;
-      w[W_SEQ] = p.s;
-      w[W_KVH] = h;
-      w[W_TOK0] = p.tok0;
-      w[W_NTOK] = p.ntok;
-      w[W_KLO] = p.klo;
-      w[W_KHI] = p.khi;
-      w[W_MODE] = p.mode;
-      w[W_GROUP] = g;
-      w[W_SPLIT] = p.split;
-      w[W_NSPLIT] = p.nsplit;
-      w[W_POFF] = poff;
-      w[W_RES] = 0;
-      if (g >= 0 && p.split == 0) {
-        int32_t *m = merge + (size_t)g * FG_WORK_INTS;
-        std::memcpy(m, w, FG_WORK_INTS * sizeof(int32_t));
-        m[W_KLO] = 0;
-        m[W_KHI] = 0;
-        m[W_SPLIT] = -1;  // marks a merge record
-      }
+      code = lst[take_tile ? it++ : nt + is++];
     }
+  }
+  for (int64_t i = 0; i < n_items; ++i) {
+    const PlanItem &p = items[i];
+    if (p.group < 0 || p.split != 0) continue;
+    for (int32_t h = 0; h < Hkv; ++h) codes[n_slots + p.group + h] = (int32_t)(i * Hkv + h);
   }
   return FG_OK;
 }

@@ -30,20 +30,22 @@ struct fg_cache {
 
 namespace fgi {
 
-// Records written by fg_attention_plan, FG_WORK_INTS int32 each.
-enum WorkField {
-  W_SEQ = 0,    // batch index s
-  W_KVH = 1,    // KV head h
-  W_TOK0 = 2,   // first query token (index into the sequence's new tokens)
-  W_NTOK = 3,   // query tokens in the record
-  W_KLO = 4,    // first key position (multiple of KEY_TILE)
-  W_KHI = 5,    // one past the last key position the record covers
-  W_MODE = 6,   // MODE_STREAM or MODE_TILE
-  W_GROUP = 7,  // split group (counter index), -1 when the record covers its whole key range
-  W_SPLIT = 8,  // split index inside the group
-  W_NSPLIT = 9, // splits in the group
-  W_POFF = 10,  // float offset of the group's partial slot 0 inside the workspace
-  W_RES = 11
+// Work items written by fg_attention_plan, FG_ITEM_INTS int32 each; record code c stands for
+// item c / Hkv and KV head c % Hkv.
+enum ItemField {
+  I_SEQ = 0,     // batch index s
+  I_TOK0 = 1,    // first query token (index into the sequence's new tokens)
+  I_NTOK = 2,    // query tokens in the item
+  I_KLO = 3,     // first key position (multiple of KEY_TILE)
+  I_KHI = 4,     // one past the last key position the item covers
+  I_MODE = 5,    // MODE_STREAM or MODE_TILE
+  I_GROUP = 6,   // split group of KV head 0 (head h: +h), -1 when the item covers its whole range
+  I_SPLIT = 7,   // split index inside the group
+  I_NSPLIT = 8,  // splits in the group
+  I_POFF = 9,    // float offset of head 0's partial slot 0 in the workspace (head h: + h *
+                 // NSPLIT * slot_floats)
+  I_RES0 = 10,
+  I_RES1 = 11
 };
 
 // MODE_STREAM: at most STREAM_ROWS query rows (decode tokens, short chunks); the four waves

@@ -138,7 +138,9 @@ __device__ __forceinline__ int swz_k(int key) { return ((key >> 1) & 12) | (key 
 __device__ __forceinline__ int swz_v(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
 struct Params {
-  const int32_t *work;
+  const int32_t *items;  // work items, FG_ITEM_INTS each
+  const int32_t *codes;  // record codes: item * Hkv + KV head, -1 for padding
+  int32_t num_items;
   const int32_t *query_start;
   const int32_t *context_len;
   const int32_t *n_query;
@@ -159,19 +161,30 @@ struct Rec {
   int s, h, tok0, ntok, klo, khi, mode, group, split, nsplit, poff;
 };
 
-__device__ __forceinline__ Rec load_rec(const int32_t *w) {
+// Record `idx`: its code names an item and a KV head.  A padding code, or one naming an item
+// outside the list, gives a record with s = -1 (the workgroup exits).
+__device__ __forceinline__ Rec load_rec(const Params &P, int idx) {
   Rec r;
-  r.s = ldc(w, W_SEQ);
-  r.h = ldc(w, W_KVH);
-  r.tok0 = ldc(w, W_TOK0);
-  r.ntok = ldc(w, W_NTOK);
-  r.klo = ldc(w, W_KLO);
-  r.khi = ldc(w, W_KHI);
-  r.mode = ldc(w, W_MODE);
-  r.group = ldc(w, W_GROUP);
-  r.split = ldc(w, W_SPLIT);
-  r.nsplit = ldc(w, W_NSPLIT);
-  r.poff = ldc(w, W_POFF);
+  const int code = ldc(P.codes, idx);
+  const int item = code >= 0 ? code / P.Hkv : -1;
+  if (item < 0 || item >= P.num_items) {
+    r.s = -1;
+    r.group = -1;
+    return r;
+  }
+  const int32_t *w = P.items + (size_t)item * FG_ITEM_INTS;
+  r.h = code - item * P.Hkv;
+  r.s = ldc(w, I_SEQ);
+  r.tok0 = ldc(w, I_TOK0);
+  r.ntok = ldc(w, I_NTOK);
+  r.klo = ldc(w, I_KLO);
+  r.khi = ldc(w, I_KHI);
+  r.mode = ldc(w, I_MODE);
+  r.split = ldc(w, I_SPLIT);
+  r.nsplit = ldc(w, I_NSPLIT);
+  const int g0 = ldc(w, I_GROUP);
+  r.group = g0 >= 0 ? g0 + r.h : -1;
+  r.poff = g0 >= 0 ? ldc(w, I_POFF) + r.h * r.nsplit * (int)slot_floats(r.mode, D) : 0;
   return r;
 }
 
@@ -275,14 +288,6 @@ __device__ void merge_splits(const Params &P, const Rec &R) {
   }
 }
 
-// Address of key `key` of KV head h (K pool) and of the 8-key run starting at `key` for
-// feature 0 (V pool).  BIG: blocks hold >= 64 keys, so a 64-key tile lies in one block and
-// keys past the sequence end still sit inside an allocated block.
-template <bool BIG>
-__device__ __forceinline__ int tile_block(const Params &P, const int32_t *bt, int k0) {
-  return BIG ? clamp_block(ldc(bt, k0 >> P.bs_log2), P.num_blocks) : 0;
-}
-
 // ---------------------------------------------------------------------------------------
 // MODE_STREAM: <= 16 query rows.  Each wave streams its own key tiles (w, w+4, ...) straight
 // from HBM into MFMA operand registers (no LDS staging, no barriers), then the four waves
@@ -316,9 +321,39 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
   for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int t_begin = R.klo / KT, t_end = (R.khi + KT - 1) / KT;
+  // Block ids are read one tile ahead (raw, clamped where used), so that a tile's K/V loads
+  // never wait behind a fresh block-table read: the two latencies would add up per tile.
+  // BIG: one scalar id per tile; otherwise per lane, for its four K rows and two V runs.
+  auto k_key = [&](int k0, int kh, int a) {
+    return min(k0 + 32 * kh + 8 * (r >> 2) + 4 * a + (r & 3), L - 1);
+  };
+  auto v_key = [&](int k0, int kh) { return min(k0 + 32 * kh + 8 * g, (L - 1) & ~7); };
+  int id_t = 0, id_k[2][2] = {{0, 0}, {0, 0}}, id_v[2] = {0, 0};
+  auto read_ids = [&](int kt) {
+    const int k0 = kt * KT;
+    if (BIG) {
+      id_t = ldc(bt, k0 >> P.bs_log2);
+    } else {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) id_k[kh][a] = bt[k_key(k0, kh, a) >> P.bs_log2];
+        id_v[kh] = bt[v_key(k0, kh) >> P.bs_log2];
+      }
+    }
+  };
+  if (t_begin + w < t_end) read_ids(t_begin + w);
   for (int kt = t_begin + w; kt < t_end; kt += NW) {
     const int k0 = kt * KT;
-    const int blk_t = tile_block<BIG>(P, bt, k0);
+    const int blk_t = BIG ? clamp_block(id_t, P.num_blocks) : 0;
+    int blk_k[2][2], blk_v[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) blk_k[kh][a] = clamp_block(id_k[kh][a], P.num_blocks);
+      blk_v[kh] = clamp_block(id_v[kh], P.num_blocks);
+    }
+    if (kt + NW < t_end) read_ids(kt + NW);
     // ---- K operand: key rows permuted so the S^T layout feeds P.V directly ------------
     bf16x8 kf[2][2][D / 32];
 #pragma unroll
@@ -328,8 +363,8 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
         int key = k0 + 32 * kh + 8 * (r >> 2) + 4 * a + (r & 3);
         int blk = blk_t;
         if (!BIG) {
-          key = min(key, L - 1);
-          blk = clamp_block(bt[key >> P.bs_log2], P.num_blocks);
+          key = k_key(k0, kh, a);
+          blk = blk_k[kh][a];
         }
         const u16 *kp = P.k_pool + ((size_t)blk * P.Hkv + R.h) * head_stride +
                         (size_t)(key & bs_mask) * D + 8 * g;
@@ -343,8 +378,8 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
       const int key0 = k0 + 32 * kh + 8 * g;
       int keyc = key0, blk = blk_t;
       if (!BIG) {
-        keyc = min(key0, (L - 1) & ~7);
-        blk = clamp_block(bt[keyc >> P.bs_log2], P.num_blocks);
+        keyc = v_key(k0, kh);
+        blk = blk_v[kh];
       }
       const u16 *vp = P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (keyc & bs_mask) +
                       (size_t)r * P.bs;
@@ -814,7 +849,7 @@ template <int BSC>
 __global__ __launch_bounds__(NT, 2) void attention_bf16_kernel(Params P) {
   __shared__ __attribute__((aligned(16))) u16 ring[NSTAGE * STAGE_ELEMS];
   __shared__ int blk_ids[MAX_IDS];
-  const Rec R = load_rec(P.work + (size_t)blockIdx.x * FG_WORK_INTS);
+  const Rec R = load_rec(P, blockIdx.x);
   if (R.s < 0 || !rec_fits_workspace(P, R)) return;  // never write outside the workspace
   Lds S;
   S.base = ring;
@@ -827,7 +862,7 @@ __global__ __launch_bounds__(NT, 2) void attention_bf16_kernel(Params P) {
 
 // Merge records follow the attention records in the work list, one per split group.
 __global__ __launch_bounds__(NT) void attention_combine_kernel(Params P, int32_t first) {
-  const Rec R = load_rec(P.work + ((size_t)first + blockIdx.x) * FG_WORK_INTS);
+  const Rec R = load_rec(P, first + blockIdx.x);
   if (R.s < 0 || R.group < 0 || !rec_fits_workspace(P, R)) return;
   merge_splits(P, R);
 }
@@ -1043,7 +1078,8 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
       return fail(FG_E_ARG, "plan was made for another batch (Hq %d, T %d)", plan->num_q_heads,
                   plan->num_tokens);
     if (plan->num_work < 1 || !work_dev || plan->num_groups < 0 ||
-        plan->num_groups >= plan->num_work)
+        plan->num_groups >= plan->num_work || plan->num_items < 1 ||
+        plan->work_ints != plan->num_items * FG_ITEM_INTS + plan->num_work)
       return fail(FG_E_ARG, "empty, null or inconsistent work list");
     if (plan->workspace_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan->workspace_bytes))
       return fail(FG_E_WORKSPACE, "workspace of %zu bytes, plan needs %lld", workspace_bytes,
@@ -1053,7 +1089,9 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
       return fail(FG_E_UNSUPPORTED, "bf16 attention reads 8-key runs: block_size %d < 8",
                   c.block_size);
     Params P;
-    P.work = work_dev;
+    P.items = work_dev;
+    P.codes = work_dev + (size_t)plan->num_items * FG_ITEM_INTS;
+    P.num_items = plan->num_items;
     P.query_start = dev->query_start;
     P.context_len = dev->context_len;
     P.n_query = dev->n_query;

@@ -15,7 +15,7 @@ import os
 import numpy as np
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfg.so")
-FG_WORK_INTS = 12
+FG_ITEM_INTS = 12
 
 FG_OK, FG_E_ARG, FG_E_DESC, FG_E_NO_BLOCKS, FG_E_UNSUPPORTED, FG_E_HIP, FG_E_WORKSPACE = range(7)
 FG_F32, FG_BF16 = 0, 1
@@ -55,7 +55,8 @@ class FgRaggedBatch(ctypes.Structure):
 class FgPlanInfo(ctypes.Structure):
     _fields_ = [("num_work", ctypes.c_int32), ("num_groups", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64),
-                ("num_q_heads", ctypes.c_int32), ("num_tokens", ctypes.c_int32)]
+                ("num_q_heads", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("num_items", ctypes.c_int32), ("work_ints", ctypes.c_int32)]
 
 
 class FgError(RuntimeError):
@@ -261,23 +262,25 @@ def fg_validate_batch(handle, batch: HostBatch):
 
 
 def fg_attention_plan(handle, batch: HostBatch, num_q_heads: int, num_cus: int, work=None):
-    """Returns (FgPlanInfo, work records as an int32 array [num_work][FG_WORK_INTS]).
+    """Returns (FgPlanInfo, the work list as a flat int32 array of info.work_ints).
 
-    ``work`` may be a reusable int32 [capacity][FG_WORK_INTS] buffer; the returned records
-    are a view of it when it is large enough (one call), else a new array (two calls)."""
+    The list is info.num_items items of FG_ITEM_INTS int32, then info.num_work record codes
+    (include/fg.h).  ``work`` may be a reusable 1-D int32 buffer; the returned list is a view
+    of it when it is large enough (one call), else a new array (two calls)."""
     info = FgPlanInfo()
-    cap = 0 if work is None else int(work.shape[0])
+    cap = 0 if work is None else int(work.size)
     st = lib().fg_attention_plan(handle, ctypes.byref(batch.c), int(num_q_heads), int(num_cus),
                                  ctypes.byref(info), _addr(work) if cap else None, cap)
-    if st == FG_OK and info.num_work <= cap:
-        return info, (work[:info.num_work] if work is not None
-                      else np.zeros((0, FG_WORK_INTS), np.int32))
-    if st not in (FG_OK, FG_E_ARG) or info.num_work <= cap:
+    if st == FG_OK and info.work_ints == 0:
+        return info, np.zeros(0, np.int32)
+    if st == FG_OK and info.work_ints <= cap:
+        return info, work.reshape(-1)[:info.work_ints]
+    if st not in (FG_OK, FG_E_ARG) or info.work_ints <= cap:
         _check(st)
-    work = np.zeros((max(info.num_work, 1), FG_WORK_INTS), np.int32)
+    work = np.zeros(max(info.work_ints, 1), np.int32)
     _check(lib().fg_attention_plan(handle, ctypes.byref(batch.c), int(num_q_heads), int(num_cus),
-                                   ctypes.byref(info), _addr(work), info.num_work))
-    return info, work[:info.num_work]
+                                   ctypes.byref(info), _addr(work), info.work_ints))
+    return info, work[:info.work_ints]
 
 
 # ---- device work ------------------------------------------------------------------------

@@ -225,6 +225,34 @@ def test_release_errors_and_reuse_order():
     fg.fg_blocked_cache_release(h, [0, 1])
     assert fg.fg_blocked_cache_free_ids(h).tolist() == [1, 0, 5, 4]         # last released first
     assert fg.fg_blocked_cache_num_free(h) == 4
+    # a bad id late in the list leaves nothing released (the marks made before it are undone)
+    assert _status(fg.fg_blocked_cache_release, h, [2, 3, 2]) == fg.FG_E_ARG
+    assert _status(fg.fg_blocked_cache_release, h, [2, 3, 7]) == fg.FG_E_ARG
+    assert fg.fg_blocked_cache_free_ids(h).tolist() == [1, 0, 5, 4]
+    fg.fg_blocked_cache_release(h, [2, 3])
+    assert fg.fg_blocked_cache_free_ids(h).tolist() == [3, 2, 1, 0, 5, 4]
+    fg.fg_blocked_cache_destroy(h)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_reverse_release_restores_the_free_list(cfg):
+    # the free list is a stack handed out from the front of free_ids: returning the k blocks
+    # a pass took, last taken first, restores it exactly (bench.py resets each step this way)
+    w = wl.make(cfg)
+    free = np.asarray(w.free_ids, np.int32)
+    h = fg.fg_blocked_cache_init(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                                 w.dtype, None, None, free)
+    before = fg.fg_blocked_cache_free_ids(h).copy()
+    ss = fg.SeqStates(w.fresh_states(), w.table_width)
+    hb = fg.HostBatch(len(w.seqs), w.table_width)
+    assert fg.fg_splitfuse_compose(h, ss, w.budget, hb) == fg.FG_OK
+    taken = len(before) - fg.fg_blocked_cache_num_free(h)
+    assert taken > 0
+    assert sorted(free[:taken].tolist()) == sorted(
+        b for i in range(ss.n) for b in ss.blocks[i][:ss.arr[i].n_blocks]
+        if b not in w.seqs[i].blocks)
+    fg.fg_blocked_cache_release(h, free[taken - 1::-1])
+    assert np.array_equal(fg.fg_blocked_cache_free_ids(h), before)
     fg.fg_blocked_cache_destroy(h)
 
 
@@ -284,9 +312,32 @@ def _compose_c(w, budget=None):
     return h, ss, hb
 
 
+def decode_plan(info, work, hkv, head_dim=128):
+    """The work list as one row per record: (s, h, tok0, ntok, klo, khi, mode, group, split,
+    nsplit, poff of the group's slot 0); padding records have s = -1 and group = -1."""
+    ni, IW = info.num_items, fg.FG_ITEM_INTS
+    assert info.work_ints == len(work) == ni * IW + info.num_work
+    items = work[:ni * IW].reshape(ni, IW)
+    slot = {0: 16 * (head_dim + 2), 1: 128 * (head_dim + 2)}
+    recs = np.full((info.num_work, 11), -1, np.int64)
+    for r, code in enumerate(work[ni * IW:]):
+        code = int(code)
+        if code == -1:
+            continue
+        assert 0 <= code < ni * hkv
+        s, t0, nt, klo, khi, mode, g0, sp, nsp, poff0, r0, r1 = (int(x) for x in items[code // hkv])
+        h = code % hkv
+        assert r0 == 0 and r1 == 0
+        grp = g0 + h if g0 >= 0 else -1
+        poff = poff0 + h * nsp * slot[mode] if g0 >= 0 else 0
+        recs[r] = (s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff)
+    return recs
+
+
 def check_plan(hb, info, work, hq, hkv, head_dim=128):
     G = hq // hkv
     S = hb.num_seqs
+    work = decode_plan(info, work, hkv, head_dim)
     assert info.num_work == len(work) and 0 <= info.num_groups < max(info.num_work, 1)
     main, merges = work[:info.num_work - info.num_groups], work[info.num_work - info.num_groups:]
     slot = {0: 16 * (head_dim + 2), 1: 128 * (head_dim + 2)}
@@ -301,13 +352,13 @@ def check_plan(hb, info, work, hq, hkv, head_dim=128):
             assert int(rec[7]) == -1
             assert all(int(r[0]) == -1 for r in main[i::8]), "padding only at an XCD list's end"
             continue
-        s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff, _ = (int(x) for x in rec)
+        s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff = (int(x) for x in rec)
         if mode == 1 and hkv % 8 == 0:  # tile records of one (sequence, head) share an XCD
             assert xcd_of_tile_group.setdefault((s, h), i % 8) == i % 8
     for rec in main:
         if int(rec[0]) == -1:
             continue
-        s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff, _ = (int(x) for x in rec)
+        s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff = (int(x) for x in rec)
         assert 0 <= s < S and 0 <= h < hkv and nt >= 1 and sp >= 0
         assert mode == (0 if nt * G <= 16 else 1) and nt * G <= 128
         c, n = int(hb.context_len[s]), int(hb.n_query[s])
@@ -347,11 +398,12 @@ def check_plan(hb, info, work, hq, hkv, head_dim=128):
         assert a[1] <= b[0]
     if spans:
         assert spans[0][0] >= 0 and spans[-1][1] * 4 <= info.workspace_bytes
-    # one merge record per group, in group order, naming the group's rows and slots
+    # one merge record per group, in group order, naming the group's rows and slots (the
+    # record of its split 0)
     assert len(merges) == info.num_groups
     for g, rec in enumerate(merges):
-        s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff, _ = (int(x) for x in rec)
-        assert grp == g and sp == -1
+        s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff = (int(x) for x in rec)
+        assert grp == g and sp == 0
         assert groups[g] == (s, h, t0, nt, mode, nsp, poff)
 
 
@@ -397,19 +449,19 @@ def test_plan_errors():
     assert _status(fg.fg_attention_plan, h, hb, 31, 256) == fg.FG_E_ARG       # Hq % Hkv
     assert _status(fg.fg_attention_plan, h, hb, 32, 0) == fg.FG_E_ARG        # no CUs
     info = fg.FgPlanInfo()
-    work = np.zeros((1, 12), np.int32)
+    work = np.zeros(12, np.int32)
     st = fg.lib().fg_attention_plan(h, ctypes.byref(hb.c), 32, 256, ctypes.byref(info),
-                                    work.ctypes.data_as(fg.i32p), 1)
-    assert st == fg.FG_E_ARG and info.num_work > 1                            # capacity
+                                    work.ctypes.data_as(fg.i32p), 12)
+    assert st == fg.FG_E_ARG and info.work_ints > 12                          # capacity
     fg.fg_blocked_cache_destroy(h)
 
 
 def test_plan_fp32_needs_no_records():
     w = wl.make(1)
     h, ss, hb = _compose_c(w)
-    for buf in (None, np.zeros((8, fg.FG_WORK_INTS), np.int32)):
+    for buf in (None, np.zeros(96, np.int32)):
         info, work = fg.fg_attention_plan(h, hb, w.num_q_heads, 256, buf)
-        assert info.num_work == 0 and work.shape == (0, fg.FG_WORK_INTS)
+        assert info.num_work == 0 and info.work_ints == 0 and work.shape == (0,)
         assert info.num_tokens == hb.num_tokens and info.workspace_bytes == 0
     fg.fg_blocked_cache_destroy(h)
 
@@ -418,10 +470,10 @@ def test_plan_reuses_a_large_enough_buffer():
     w = wl.make(2)
     h, ss, hb = _compose_c(w)
     info0, work0 = fg.fg_attention_plan(h, hb, 32, 256)
-    buf = np.zeros((info0.num_work + 5, fg.FG_WORK_INTS), np.int32)
+    buf = np.zeros(info0.work_ints + 5, np.int32)
     info1, work1 = fg.fg_attention_plan(h, hb, 32, 256, buf)
     assert work1.base is buf and np.array_equal(work0, work1)
-    small = np.zeros((3, fg.FG_WORK_INTS), np.int32)
+    small = np.zeros(36, np.int32)
     info2, work2 = fg.fg_attention_plan(h, hb, 32, 256, small)
     assert np.array_equal(work0, work2)
     fg.fg_blocked_cache_destroy(h)
