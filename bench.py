@@ -11,6 +11,13 @@ Default workload: LLaMA-2-7B attention shape (32 heads of 128, blocks of 64), a 
 budget filled by 24 decode tokens plus prompt chunks.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2|decode|chunked|mistral]
+
+`--workload serving` instead runs the multi-pass serving loop (continuous batching over
+SplitFuse passes) on the whole request stream -- 512 requests from `--clients` closed-loop
+clients, prompt and output lengths normal with means 2600 and 60 -- once untimed and once
+timed, and reports the run's tokens/s plus per-request latencies in passes and seconds.
+
+    python bench.py --workload serving [--clients 32] [--requests 512] [--budget 2048]
 """
 import argparse
 import ctypes
@@ -27,7 +34,7 @@ METRIC = "ragged-pass tokens/s at fixed budget; KV HBM GB/s & MFMA % of peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 F32_VALU_PEAK_TFLOPS = 157.3
-WORKLOADS = {"llama2": 2, "decode": 3, "chunked": 4, "mistral": 5}
+WORKLOADS = {"llama2": 2, "decode": 3, "chunked": 4, "mistral": 5, "serving": 0}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 
 
@@ -52,6 +59,11 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--num-cus", type=int, default=0,
                     help="compute units the attention planner sizes splits for (0 = device's)")
+    ap.add_argument("--clients", type=int, default=32, help="serving: closed-loop clients")
+    ap.add_argument("--requests", type=int, default=512, help="serving: requests in the stream")
+    ap.add_argument("--budget", type=int, default=2048, help="serving: token budget per pass")
+    ap.add_argument("--model", default="llama2", choices=["llama2", "mistral"],
+                    help="serving: attention shape (LLaMA-2-7B 32/32 or Mistral-7B 32/8 heads)")
     return ap.parse_args()
 
 
@@ -99,6 +111,9 @@ def main():
     from ragged_blocked_kv_splitfuse_amd.runtime import DeviceDescriptors, Workspace, stream_handle
 
     torch.cuda.set_device(0)
+    if args.workload == "serving":
+        serving_main(args)
+        return
     S = setup(args)
     w, cache, ss, hb = S["w"], S["cache"], S["ss"], S["hb"]
     arr_bytes, blocks0 = S["template"]
@@ -226,6 +241,98 @@ def main():
                     "gpu_only_tokens_per_s": T / (t_attn + t_app),
                     "host_us_per_step": float(np.mean(host_s[args.warmup:])) * 1e6},
         "cpu_baseline": cpu_baseline(args, w, cache, hb, q, k_new, v_new) if args.cpu_seconds > 0 else None,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def serving_main(args):
+    """The serving loop over the whole request stream: one untimed run, one timed run, each
+    from the same initial pool state (a fresh cache handle over the same pools)."""
+    import numpy as np
+    import torch
+    from ragged_blocked_kv_splitfuse_amd import fg, workloads as wl
+    from ragged_blocked_kv_splitfuse_amd.runtime import PagedKVCache, num_cus
+    from ragged_blocked_kv_splitfuse_amd.serving import DevicePass, ServingLoop
+
+    hkv = 32 if args.model == "llama2" else 8
+    sw = wl.serving_stream(seed=args.seed if args.seed is not None else 6,
+                           n_requests=args.requests, clients=args.clients, budget=args.budget,
+                           hkv=hkv, name=f"serving_{args.model}_7b")
+    v = sw.values
+    tdt = torch.bfloat16
+    cache = PagedKVCache(v.num_blocks, v.block_size, v.num_kv_heads, v.head_dim, v.dtype,
+                         free_ids=v.free_ids)
+    wl.fill_pools_device(cache.k_pool, cache.v_pool, seed=v.seed * 7919 + 1)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(v.seed * 104729 + 17)
+    mk = lambda heads: torch.randn((sw.budget, heads, v.head_dim), generator=g,
+                                   device="cuda").to(tdt)
+    q, kn, vn = mk(v.num_q_heads), mk(v.num_kv_heads), mk(v.num_kv_heads)
+    cus = args.num_cus or num_cus()
+
+    def run(timed):
+        h = fg.fg_blocked_cache_init(v.num_blocks, v.block_size, v.num_kv_heads, v.head_dim,
+                                     v.dtype, cache.k_pool.data_ptr(), cache.v_pool.data_ptr(),
+                                     v.free_ids)
+        class Handle:   # DevicePass wants the handle's owner: the same pools, this handle
+            handle, head_dim = h, v.head_dim
+
+        dp = DevicePass(Handle, v.num_q_heads, v.scale,
+                        lambda hb, running: (q[:hb.num_tokens], kn[:hb.num_tokens],
+                                             vn[:hb.num_tokens]), cus, timing=timed)
+        try:
+            loop = ServingLoop(h, v.block_size, sw.budget, sw.clients, sw.table_width)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            st = loop.run(sw.requests, device_pass=dp)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        finally:
+            fg.fg_blocked_cache_destroy(h)
+        marks = dp.marks
+        return st, wall, marks
+
+    run(False)
+    st, wall, marks = run(True)
+    app = np.array([a.elapsed_time(b) for a, b, _ in marks]) * 1e-3
+    att = np.array([b.elapsed_time(c) for _, b, c in marks]) * 1e-3
+    ends = np.array([marks[0][0].elapsed_time(c) for _, _, c in marks]) * 1e-3
+    T = np.array(st.tokens)
+    total = int(T.sum())
+    # latencies: a request joins when the pass before its admission pass ended (or at the
+    # start); its first token comes with the end of its first-token pass
+    start = lambda p: 0.0 if p == 0 else float(ends[p - 1])
+    ttft_p, ttft_s, pace_s = [], [], []
+    for r in sw.requests:
+        a, f, e = st.admit_pass[r.rid], st.first_token_pass[r.rid], st.finish_pass[r.rid]
+        ttft_p.append(f - a + 1)
+        ttft_s.append(float(ends[f]) - start(a))
+        if r.output_len > 1:
+            pace_s.append((float(ends[e]) - float(ends[f])) / (r.output_len - 1))
+    result = {
+        "metric": "serving-loop tokens/s (continuous SplitFuse passes, whole request stream)",
+        "value": total / wall, "unit": "tokens/s", "n_gpus": 1, "steps": st.passes,
+        "warmup": 1, "ms_per_step": wall / st.passes * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": sw.name, "requests": len(sw.requests), "clients": sw.clients,
+                   "token_budget": sw.budget, "q_heads": v.num_q_heads,
+                   "kv_heads": v.num_kv_heads, "head_dim": v.head_dim,
+                   "block_size": v.block_size, "pool_blocks": v.num_blocks,
+                   "prompt_mean": 2600, "output_mean": 60, "cv": 0.3},
+        "serving": {"passes": st.passes, "tokens": total,
+                    "full_budget_passes": int((T == sw.budget).sum()),
+                    "mean_T": float(T.mean()), "mean_S": float(np.mean(st.seqs)),
+                    "gpu_s": float(app.sum() + att.sum()), "wall_s": wall,
+                    "gpu_only_tokens_per_s": total / float(app.sum() + att.sum()),
+                    "attention_us_mean": float(att.mean() * 1e6),
+                    "kv_append_us_mean": float(app.mean() * 1e6),
+                    "ttft_passes_mean": float(np.mean(ttft_p)),
+                    "ttft_ms_mean": float(np.mean(ttft_s) * 1e3),
+                    "ttft_ms_p95": float(np.percentile(ttft_s, 95) * 1e3),
+                    "token_pace_ms_mean": float(np.mean(pace_s) * 1e3),
+                    "token_pace_ms_p95": float(np.percentile(pace_s, 95) * 1e3)},
+        "roofline": None,
+        "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)
 

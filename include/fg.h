@@ -80,7 +80,9 @@ typedef struct fg_seq_state {
   int32_t max_blocks;  /* capacity of blocks[]; the sequence never owns more */
   int32_t *blocks;     /* physical ids in logical order (in/out), capacity max_blocks */
   int32_t n_scheduled; /* out: tokens given to this sequence in the composed pass */
-  int32_t reserved;
+  int32_t stop_len;    /* > 0: the request is done once n_cached >= stop_len (a prompt of P
+                          tokens and O generated tokens caches P + O - 1 positions); 0: never
+                          done (fg_splitfuse_retire leaves it alone) */
 } fg_seq_state;
 
 /* Ragged batch descriptor.  The struct itself is always host memory; its arrays are host
@@ -150,6 +152,19 @@ fg_status fg_splitfuse_compose(fg_cache *cache, fg_seq_state *seqs, int32_t n_se
                                int32_t token_budget, fg_ragged_batch *out);
 /* After the pass ran: n_cached += n_scheduled, n_scheduled = 0, for every sequence. */
 fg_status fg_splitfuse_commit(fg_seq_state *seqs, int32_t n_seqs);
+
+/* Continuous batching (blog "1. Introduction" and the paper card's "Key points": requests
+ * join and leave the running set between passes, the blocked KV cache recycling the blocks
+ * of finished ones).  Call after fg_splitfuse_commit.  Every sequence with stop_len > 0 and
+ * n_cached >= stop_len is retired: its blocks go back to the free list -- retired sequences
+ * in array order, each one's blocks in logical order, so the last block of the last retired
+ * sequence is handed out first -- and its n_blocks becomes 0.  The array is then stably
+ * partitioned: live sequences first (their order kept), the retired ones after them (theirs
+ * kept), so seqs[*n_live..n_seqs) are the retired entries, whose blocks storage the caller
+ * may reuse for new requests.  Errors: FG_E_ARG (null pointers, a sequence with blocks but
+ * no storage, a block id out of range, already free or owned twice); then nothing changed. */
+fg_status fg_splitfuse_retire(fg_cache *cache, fg_seq_state *seqs, int32_t n_seqs,
+                              int32_t *n_live);
 
 /* Full O(S * table_stride) check of a host batch: prefix sums, n_query >= 1, every block a
  * valid id, no id used twice, enough blocks for context_len + n_query.  FG_E_DESC names the

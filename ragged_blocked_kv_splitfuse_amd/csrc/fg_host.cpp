@@ -248,6 +248,31 @@ fg_status fg_splitfuse_commit(fg_seq_state *seqs, int32_t n_seqs) {
   return FG_OK;
 }
 
+static bool seq_done(const fg_seq_state &s) { return s.stop_len > 0 && s.n_cached >= s.stop_len; }
+
+fg_status fg_splitfuse_retire(fg_cache *cache, fg_seq_state *seqs, int32_t n_seqs,
+                              int32_t *n_live) {
+  clear_error();
+  if (!cache || !n_live) return fail(FG_E_ARG, "null cache or n_live");
+  if (n_seqs < 0 || (n_seqs > 0 && !seqs)) return fail(FG_E_ARG, "bad sequence array");
+  std::vector<int32_t> ids;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const fg_seq_state &s = seqs[i];
+    if (!seq_done(s)) continue;
+    if (s.n_blocks < 0 || (s.n_blocks > 0 && !s.blocks))
+      return fail(FG_E_ARG, "sequence %d: inconsistent blocks", i);
+    ids.insert(ids.end(), s.blocks, s.blocks + s.n_blocks);
+  }
+  // one release for all of them: it checks every id first, so an error changes nothing
+  const fg_status st = fg_blocked_cache_release(cache, ids.data(), (int32_t)ids.size());
+  if (st != FG_OK) return st;
+  fg_seq_state *mid = std::stable_partition(
+      seqs, seqs + n_seqs, [](const fg_seq_state &s) { return !seq_done(s); });
+  for (fg_seq_state *p = mid; p != seqs + n_seqs; ++p) p->n_blocks = 0;
+  *n_live = (int32_t)(mid - seqs);
+  return FG_OK;
+}
+
 // --------------------------------------------------------------------------------------
 // validation
 // --------------------------------------------------------------------------------------

@@ -24,7 +24,7 @@ DTYPES = {"f32": FG_F32, "bf16": FG_BF16}
 EXPORTS = [
     "fg_blocked_cache_init", "fg_blocked_cache_destroy", "fg_blocked_cache_num_free",
     "fg_blocked_cache_free_ids", "fg_blocked_cache_release", "fg_splitfuse_compose",
-    "fg_splitfuse_commit", "fg_validate_batch", "fg_kv_append", "fg_attention_plan",
+    "fg_splitfuse_commit", "fg_splitfuse_retire", "fg_validate_batch", "fg_kv_append", "fg_attention_plan",
     "fg_ragged_attention", "fg_status_string", "fg_last_error",
 ]
 
@@ -42,7 +42,7 @@ class FgSeqState(ctypes.Structure):
     _fields_ = [("seq_id", ctypes.c_int64), ("n_cached", ctypes.c_int32),
                 ("prompt_len", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
                 ("max_blocks", ctypes.c_int32), ("blocks", i32p),
-                ("n_scheduled", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("n_scheduled", ctypes.c_int32), ("stop_len", ctypes.c_int32)]
 
 
 class FgRaggedBatch(ctypes.Structure):
@@ -103,6 +103,7 @@ def _declare(L):
         "fg_splitfuse_compose": ([vp, ctypes.POINTER(FgSeqState), ctypes.c_int32, ctypes.c_int32,
                                   ctypes.POINTER(FgRaggedBatch)], st),
         "fg_splitfuse_commit": ([ctypes.POINTER(FgSeqState), ctypes.c_int32], st),
+        "fg_splitfuse_retire": ([vp, ctypes.POINTER(FgSeqState), ctypes.c_int32, i32p], st),
         "fg_validate_batch": ([vp, ctypes.POINTER(FgRaggedBatch)], st),
         "fg_kv_append": ([vp, ctypes.POINTER(FgRaggedBatch), vp, vp, vp], st),
         "fg_attention_plan": ([vp, ctypes.POINTER(FgRaggedBatch), ctypes.c_int32, ctypes.c_int32,
@@ -210,6 +211,7 @@ class SeqStates:
             a.max_blocks = per_seq[i]
             a.blocks = ctypes.cast(_addr(self.blocks) + i * self.blocks.strides[0], i32p)
             a.n_scheduled = 0
+            a.stop_len = int(getattr(s, "stop_len", 0))
 
     def n_cached(self, i):
         return int(self.arr[i].n_cached)
@@ -255,6 +257,13 @@ def fg_splitfuse_compose(handle, seqs: SeqStates, token_budget: int, out: HostBa
 
 def fg_splitfuse_commit(seqs: SeqStates):
     _check(lib().fg_splitfuse_commit(seqs.arr, seqs.n))
+
+
+def fg_splitfuse_retire(handle, arr, n: int) -> int:
+    """Retire finished sequences of the fg_seq_state array ``arr[0..n)``; returns n_live."""
+    n_live = ctypes.c_int32(0)
+    _check(lib().fg_splitfuse_retire(handle, arr, int(n), ctypes.byref(n_live)))
+    return int(n_live.value)
 
 
 def fg_validate_batch(handle, batch: HostBatch):

@@ -236,6 +236,73 @@ def custom(seed, *, dtype="bf16", hq=8, hkv=8, d=128, bs=64, budget=256, n_decod
     return w
 
 
+# ---------------------------------------------------------------------------
+# request streams for the multi-pass serving loop
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Request:
+    rid: int           # also the sequence id of its value streams
+    prompt_len: int    # P >= 1
+    output_len: int    # O >= 1 generated tokens
+
+    @property
+    def stop_len(self) -> int:
+        """Positions whose K/V the request caches: its P prompt tokens and the first O - 1
+        generated ones (the last generated token is never fed back)."""
+        return self.prompt_len + self.output_len - 1
+
+
+@dataclass
+class ServingWorkload:
+    """Requests of `clients` closed-loop clients: client c sends requests c, c + clients,
+    c + 2*clients, ... one at a time, the next as soon as the previous finished."""
+    name: str
+    requests: list
+    clients: int
+    budget: int
+    values: Workload        # shapes, value streams (keyed by request id) and pool size
+
+    @property
+    def table_width(self) -> int:
+        bs = self.values.block_size
+        return max(-(-r.stop_len // bs) for r in self.requests)
+
+
+def serving_stream(seed: int = 6, n_requests: int = 512, clients: int = 32, budget: int = 2048,
+                   prompt_mean: float = 2600.0, output_mean: float = 60.0, cv: float = 0.3,
+                   prompt_clip=(64, 8192), output_clip=(1, 512), dtype: str = "bf16",
+                   hq: int = 32, hkv: int = 32, d: int = 128, bs: int = 64,
+                   value_scale: float = 1.0, name: str = "serving_llama2_7b") -> ServingWorkload:
+    """The card's request stream ("Key points": prompt and generation lengths normal with
+    means 2600 and 60 and a 30% coefficient of variation; 1 to 32 clients; 512 requests), at
+    an attention shape of the model families it names (LLaMA-2-7B by default).  The pool
+    holds the largest possible running set: `clients` requests of the largest block count."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    P = _normal_len(rng, prompt_mean, cv * prompt_mean, prompt_clip[0], prompt_clip[1],
+                    size=n_requests)
+    O = _normal_len(rng, output_mean, cv * output_mean, output_clip[0], output_clip[1],
+                    size=n_requests)
+    reqs = [Request(10000 + i, int(p), int(o)) for i, (p, o) in enumerate(zip(P, O))]
+    width = max(-(-r.stop_len // bs) for r in reqs)
+    nb = min(clients, n_requests) * width
+    free = rng.permutation(nb).astype(np.int32)
+    vals = Workload(name=name, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                    block_size=bs, num_blocks=nb, budget=budget, scale=1.0 / math.sqrt(d),
+                    value_scale=value_scale, seed=seed, seqs=[], free_ids=free,
+                    table_width=width)
+    return ServingWorkload(name=name, requests=reqs, clients=int(clients), budget=int(budget),
+                           values=vals)
+
+
+def serving_small(seed: int = 7, dtype: str = "bf16", n_requests: int = 10, clients: int = 3,
+                  budget: int = 96, bs: int = 16) -> ServingWorkload:
+    """A small stream for parity: prompts ~N(120, 36), outputs ~N(6, 2), 4 query heads over
+    2 KV heads of 128."""
+    return serving_stream(seed, n_requests, clients, budget, 120.0, 6.0, 0.3, (8, 400), (1, 20),
+                          dtype, 4, 2, 128, bs, 1.0, "serving_small")
+
+
 CONFIGS = {
     1: tiny_f32,
     2: llama2_mixed,
