@@ -18,6 +18,10 @@ clients, prompt and output lengths normal with means 2600 and 60 -- once untimed
 timed, and reports the run's tokens/s plus per-request latencies in passes and seconds.
 
     python bench.py --workload serving [--clients 32] [--requests 512] [--budget 2048]
+
+`--workload sweep` times the pass over shape sweeps (sequence count at a fixed token count;
+token budget for one prompt chunk and for decode tokens) and prints one JSON line with every
+point.
 """
 import argparse
 import ctypes
@@ -34,7 +38,7 @@ METRIC = "ragged-pass tokens/s at fixed budget; KV HBM GB/s & MFMA % of peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 F32_VALU_PEAK_TFLOPS = 157.3
-WORKLOADS = {"llama2": 2, "decode": 3, "chunked": 4, "mistral": 5, "serving": 0}
+WORKLOADS = {"llama2": 2, "decode": 3, "chunked": 4, "mistral": 5, "serving": 0, "sweep": 0}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 
 
@@ -86,6 +90,14 @@ def setup(args):
         init_states[0].n_cached = c
         init_states[0].blocks = order[:nb].tolist()
         free_ids = order[nb:]
+    return prepare(w, init_states, free_ids, args.num_cus or num_cus())
+
+
+def prepare(w, init_states, free_ids, cus):
+    """Pools on the device (filled with seeded values), sequence states and a host batch."""
+    import torch
+    from ragged_blocked_kv_splitfuse_amd import fg, workloads as wl
+    from ragged_blocked_kv_splitfuse_amd.runtime import PagedKVCache
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     cache = PagedKVCache(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype,
                          free_ids=free_ids)
@@ -95,26 +107,60 @@ def setup(args):
     template = (bytes(ss.arr), ss.blocks.copy())
     hb = fg.HostBatch(ss.n, w.table_width)
     return dict(w=w, cache=cache, ss=ss, template=template, hb=hb, free_ids=free_ids,
-                cus=args.num_cus or num_cus(), tdt=tdt)
+                cus=cus, tdt=tdt)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
-              "multi-GPU path; the pass shards by KV head or by sequence with no exchange "
-              "inside it, see the design notes.", file=sys.stderr)
-        sys.exit(2)
+# The profiling sweeps: (S, n, c) = sequences, new tokens each, cached tokens each.
+SWEEP_S = [(S, 2048 // S, 1024) for S in (1, 4, 16, 64, 256, 1024, 2048)]
+SWEEP_T_CHUNK = [(1, T, 2048) for T in (64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384)]
+SWEEP_T_DECODE = [(T, 1, 1024) for T in (16, 64, 256, 1024, 2048)]
+
+
+def sweep_main(args):
+    """Latency and throughput of the pass (kv_append + attention) over the three shape
+    families: sequence count at a fixed 2048-token pass, then the token budget for one
+    prompt chunk and for decode tokens.  One JSON line holding every point."""
+    import numpy as np
+    import torch
+    from ragged_blocked_kv_splitfuse_amd import workloads as wl
+    from ragged_blocked_kv_splitfuse_amd.runtime import num_cus
+    cus = args.num_cus or num_cus()
+    points = []
+    for family, pts in (("seqs_at_T2048", SWEEP_S), ("budget_one_chunk", SWEEP_T_CHUNK),
+                        ("budget_decodes", SWEEP_T_DECODE)):
+        for S_, n, c in pts:
+            w = wl.uniform_pass(S_, n, c)
+            P = prepare(w, w.fresh_states(), np.asarray(w.free_ids, np.int32), cus)
+            r = time_pass(P, args.steps, args.warmup)
+            t = r["t_attn"] + r["t_app"]
+            points.append({"family": family, "S": S_, "n": n, "c": c, "T": r["T"],
+                           "attention_us": r["t_attn"] * 1e6, "kv_append_us": r["t_app"] * 1e6,
+                           "pass_us": t * 1e6, "tokens_per_s": r["T"] / t,
+                           "step_us": r["elapsed"] / args.steps * 1e6,
+                           "attn_flops": r["attn_flops"], "attn_bytes": r["attn_bytes"],
+                           "mfma_frac": r["attn_flops"] / r["t_attn"] / 1e12 / BF16_PEAK_TFLOPS,
+                           "hbm_frac": r["attn_bytes"] / r["t_attn"] / 1e9 / HBM_PEAK_GBS})
+            print(json.dumps({"point": points[-1]}), file=sys.stderr, flush=True)
+            del P, r
+            torch.cuda.empty_cache()
+    print(json.dumps({"metric": "pass latency and tokens/s over shape sweeps", "unit": "us",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+                      "data": "synthetic",
+                      "config": {"workload": "uniform passes, LLaMA-2-7B attention shape",
+                                 "q_heads": 32, "kv_heads": 32, "head_dim": 128,
+                                 "block_size": 64},
+                      "points": points}), flush=True)
+
+
+def time_pass(S, steps, warmup):
+    """Warm up, then time `steps` identical passes (compose + plan + upload + kv_append +
+    attention) of the prepared workload.  Kernel times come from HIP events on the launch
+    stream; `elapsed` is the host clock over the timed steps, bracketed by synchronizations."""
     import numpy as np
     import torch
     from ragged_blocked_kv_splitfuse_amd import fg
     from ragged_blocked_kv_splitfuse_amd.runtime import DeviceDescriptors, Workspace, stream_handle
 
-    torch.cuda.set_device(0)
-    if args.workload == "serving":
-        serving_main(args)
-        return
-    S = setup(args)
     w, cache, ss, hb = S["w"], S["cache"], S["ss"], S["hb"]
     arr_bytes, blocks0 = S["template"]
     free_ids = S["free_ids"]
@@ -140,7 +186,7 @@ def main():
         st = fg.fg_splitfuse_compose(h, ss, w.budget, hb)
         assert st == fg.FG_OK
         info, work = fg.fg_attention_plan(h, hb, w.num_q_heads, S["cus"], work_buf)
-        return h, info, work
+        return info, work
 
     def restore_free_list():
         taken = n_free0 - fg.fg_blocked_cache_num_free(h)
@@ -148,7 +194,7 @@ def main():
             fg.fg_blocked_cache_release(h, free_ids[taken - 1::-1])
 
     # pass shape and inputs
-    h, info, work = compose_and_plan()
+    info, work = compose_and_plan()
     T, nseq = hb.num_tokens, hb.num_seqs
     ctx = hb.context_len[:nseq].astype(np.int64)
     nq = hb.n_query[:nseq].astype(np.int64)
@@ -168,14 +214,14 @@ def main():
     attn_flops = 4 * w.head_dim * w.num_q_heads * pairs
     append_bytes = 4 * T * w.num_kv_heads * w.head_dim * e
 
-    n_total = args.warmup + args.steps
+    n_total = warmup + steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(n_total)]
     host_s = []
 
     def step(i):
         t0 = time.perf_counter()
-        h, info, work = compose_and_plan()
+        info, work = compose_and_plan()
         c = desc.upload(hb, work, stream)
         ev[i][0].record(stream)
         fg.fg_kv_append(h, c, k_new.data_ptr(), v_new.data_ptr(), sh)
@@ -185,22 +231,53 @@ def main():
         ev[i][2].record(stream)
         restore_free_list()
         host_s.append(time.perf_counter() - t0)
+        return info
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.warmup, n_total):
-        step(i)
+    for i in range(warmup, n_total):
+        info = step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    fg.fg_blocked_cache_destroy(h)
 
-    timed = ev[args.warmup:]
+    timed = ev[warmup:]
     attn_ms = [a.elapsed_time(b2) for _, a, b2 in timed]   # attention launch only
     app_ms = [a0.elapsed_time(a) for a0, a, _ in timed]
-    t_attn = float(np.mean(attn_ms)) * 1e-3
-    t_app = float(np.mean(app_ms)) * 1e-3
-    elapsed = t1 - t0
+    return dict(info=info, T=T, nseq=nseq, nq=nq, ctx=ctx, kv_tokens=kv_tokens,
+                attn_bytes=attn_bytes, attn_flops=attn_flops, append_bytes=append_bytes,
+                t_attn=float(np.mean(attn_ms)) * 1e-3, t_app=float(np.mean(app_ms)) * 1e-3,
+                elapsed=t1 - t0, q=q, k_new=k_new, v_new=v_new, host_s=host_s[warmup:])
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path; the pass shards by KV head or by sequence with no exchange "
+              "inside it, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from ragged_blocked_kv_splitfuse_amd import fg
+    from ragged_blocked_kv_splitfuse_amd.runtime import DeviceDescriptors, Workspace, stream_handle
+
+    torch.cuda.set_device(0)
+    if args.workload == "serving":
+        serving_main(args)
+        return
+    if args.workload == "sweep":
+        sweep_main(args)
+        return
+    S = setup(args)
+    r = time_pass(S, args.steps, args.warmup)
+    w, cache, hb, info = S["w"], S["cache"], S["hb"], r["info"]
+    T, nseq, nq, kv_tokens = r["T"], r["nseq"], r["nq"], r["kv_tokens"]
+    attn_bytes, attn_flops, append_bytes = r["attn_bytes"], r["attn_flops"], r["append_bytes"]
+    t_attn, t_app, elapsed = r["t_attn"], r["t_app"], r["elapsed"]
+    q, k_new, v_new, host_s = r["q"], r["k_new"], r["v_new"], r["host_s"]
     value = T * args.steps / elapsed
 
     if w.dtype == "bf16" and args.workload != "chunked":
@@ -239,7 +316,7 @@ def main():
         "kernels": {"attention_us": t_attn * 1e6, "kv_append_us": t_app * 1e6,
                     "kv_append_GBps": append_bytes / t_app / 1e9,
                     "gpu_only_tokens_per_s": T / (t_attn + t_app),
-                    "host_us_per_step": float(np.mean(host_s[args.warmup:])) * 1e6},
+                    "host_us_per_step": float(np.mean(host_s)) * 1e6},
         "cpu_baseline": cpu_baseline(args, w, cache, hb, q, k_new, v_new) if args.cpu_seconds > 0 else None,
     }
     print(json.dumps(result), flush=True)

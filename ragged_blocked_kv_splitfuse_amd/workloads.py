@@ -236,6 +236,18 @@ def custom(seed, *, dtype="bf16", hq=8, hkv=8, d=128, bs=64, budget=256, n_decod
     return w
 
 
+def uniform_pass(S: int, n: int, c: int, seed: int = 8, hq: int = 32, hkv: int = 32,
+                 d: int = 128, bs: int = 64) -> Workload:
+    """S sequences, each with c cached tokens and n new ones (a pass of T = S*n tokens): the
+    shape family of the profiling sweeps (paper card "Interesting ideas": pass latency is
+    driven by the total token count; throughput saturates and is concave in it)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    specs = [(7000 + i, int(c), int(c + n)) for i in range(S)]
+    nb = S * -(-(c + n) // bs)
+    return _finish(f"uniform_S{S}_n{n}_c{c}", "bf16", hq, hkv, d, bs, S * n, 1.0, seed, specs,
+                   nb, rng)
+
+
 # ---------------------------------------------------------------------------
 # request streams for the multi-pass serving loop
 # ---------------------------------------------------------------------------
