@@ -68,6 +68,10 @@ def parse():
     ap.add_argument("--budget", type=int, default=2048, help="serving: token budget per pass")
     ap.add_argument("--model", default="llama2", choices=["llama2", "mistral"],
                     help="serving: attention shape (LLaMA-2-7B 32/32 or Mistral-7B 32/8 heads)")
+    ap.add_argument("--layer", action="store_true",
+                    help="serving: each pass also runs the QKV and output projections")
+    ap.add_argument("--layers", type=int, default=32,
+                    help="serving: layer count of the latency proxy (pass time x layers)")
     return ap.parse_args()
 
 
@@ -346,17 +350,28 @@ def serving_main(args):
                                    device="cuda").to(tdt)
     q, kn, vn = mk(v.num_q_heads), mk(v.num_kv_heads), mk(v.num_kv_heads)
     cus = args.num_cus or num_cus()
+    proj = None
+    if args.layer:
+        from ragged_blocked_kv_splitfuse_amd.serving import Projections
+        hid = v.num_q_heads * v.head_dim
+        wmk = lambda n: (torch.randn((n, hid), generator=g, device="cuda")
+                         / hid ** 0.5).to(tdt)
+        proj = Projections(wmk(hid), wmk(v.num_kv_heads * v.head_dim),
+                           wmk(v.num_kv_heads * v.head_dim), wmk(hid), sw.budget)
+        x = torch.randn((sw.budget, hid), generator=g, device="cuda").to(tdt)
+        rows = lambda hb, running: x[:hb.num_tokens]
+    else:
+        rows = lambda hb, running: (q[:hb.num_tokens], kn[:hb.num_tokens], vn[:hb.num_tokens])
 
     def run(timed):
         h = fg.fg_blocked_cache_init(v.num_blocks, v.block_size, v.num_kv_heads, v.head_dim,
                                      v.dtype, cache.k_pool.data_ptr(), cache.v_pool.data_ptr(),
                                      v.free_ids)
+
         class Handle:   # DevicePass wants the handle's owner: the same pools, this handle
             handle, head_dim = h, v.head_dim
 
-        dp = DevicePass(Handle, v.num_q_heads, v.scale,
-                        lambda hb, running: (q[:hb.num_tokens], kn[:hb.num_tokens],
-                                             vn[:hb.num_tokens]), cus, timing=timed)
+        dp = DevicePass(Handle, v.num_q_heads, v.scale, rows, cus, timing=timed, proj=proj)
         try:
             loop = ServingLoop(h, v.block_size, sw.budget, sw.clients, sw.table_width)
             torch.cuda.synchronize()
@@ -366,26 +381,67 @@ def serving_main(args):
             wall = time.perf_counter() - t0
         finally:
             fg.fg_blocked_cache_destroy(h)
-        marks = dp.marks
-        return st, wall, marks
+        return st, wall, dp.marks
 
     run(False)
     st, wall, marks = run(True)
-    app = np.array([a.elapsed_time(b) for a, b, _ in marks]) * 1e-3
-    att = np.array([b.elapsed_time(c) for _, b, c in marks]) * 1e-3
-    ends = np.array([marks[0][0].elapsed_time(c) for _, _, c in marks]) * 1e-3
+    seg = np.array([[m[i].elapsed_time(m[i + 1]) for i in range(4)] for m in marks]) * 1e-3
+    qkv_s, app, att, oproj_s = seg[:, 0], seg[:, 1], seg[:, 2], seg[:, 3]
+    ends = np.array([marks[0][0].elapsed_time(m[4]) for m in marks]) * 1e-3
     T = np.array(st.tokens)
     total = int(T.sum())
-    # latencies: a request joins when the pass before its admission pass ended (or at the
-    # start); its first token comes with the end of its first-token pass
-    start = lambda p: 0.0 if p == 0 else float(ends[p - 1])
-    ttft_p, ttft_s, pace_s = [], [], []
-    for r in sw.requests:
-        a, f, e = st.admit_pass[r.rid], st.first_token_pass[r.rid], st.finish_pass[r.rid]
-        ttft_p.append(f - a + 1)
-        ttft_s.append(float(ends[f]) - start(a))
-        if r.output_len > 1:
-            pace_s.append((float(ends[e]) - float(ends[f])) / (r.output_len - 1))
+    gpu_pass = seg.sum(axis=1)
+
+    def latencies(end_times):
+        """Per request: time to first token (from joining -- the end of the pass before its
+        admission pass -- to the end of its first-token pass) and the mean gap between its
+        generated tokens."""
+        start = lambda p: 0.0 if p == 0 else float(end_times[p - 1])
+        ttft, pace = [], []
+        for r in sw.requests:
+            a, f, e = st.admit_pass[r.rid], st.first_token_pass[r.rid], st.finish_pass[r.rid]
+            ttft.append(float(end_times[f]) - start(a))
+            pace.append((float(end_times[e]) - float(end_times[f])) / (r.output_len - 1)
+                        if r.output_len > 1 else np.nan)
+        return np.array(ttft), np.array(pace)
+
+    def summary(end_times):
+        ttft, pace = latencies(end_times)
+        pc = pace[~np.isnan(pace)]
+        return {"ttft_ms_mean": float(ttft.mean() * 1e3),
+                "ttft_ms_p50": float(np.percentile(ttft, 50) * 1e3),
+                "ttft_ms_p95": float(np.percentile(ttft, 95) * 1e3),
+                "token_pace_ms_mean": float(pc.mean() * 1e3),
+                "token_pace_ms_p95": float(np.percentile(pc, 95) * 1e3)}
+
+    ttft_p = [st.first_token_pass[r.rid] - st.admit_pass[r.rid] + 1 for r in sw.requests]
+    serving = {"passes": st.passes, "tokens": total,
+               "full_budget_passes": int((T == sw.budget).sum()),
+               "mean_T": float(T.mean()), "mean_S": float(np.mean(st.seqs)),
+               "gpu_s": float(gpu_pass.sum()), "wall_s": wall,
+               "gpu_only_tokens_per_s": total / float(gpu_pass.sum()),
+               "attention_us_mean": float(att.mean() * 1e6),
+               "kv_append_us_mean": float(app.mean() * 1e6),
+               "ttft_passes_mean": float(np.mean(ttft_p)), **summary(ends)}
+    if proj is not None:
+        gflops = sum(proj.flops(int(t)) for t in T)
+        gsec = float(qkv_s.sum() + oproj_s.sum())
+        serving.update({"projections_us_mean": float((qkv_s + oproj_s).mean() * 1e6),
+                        "projection_tflops": gflops / gsec / 1e12,
+                        "projection_mfma_frac": gflops / gsec / 1e12 / BF16_PEAK_TFLOPS})
+    # Latency proxy: a model of `layers` identical layers whose pass costs `layers` times the
+    # measured one (attention layer only -- no MLP, norms or sampling), on the GPU timeline.
+    L = args.layers
+    proxy_ends = np.cumsum(gpu_pass * L)
+    proxy = {"layers": L, "includes": "kv_append + attention" + (" + QKV/O projections"
+                                                                 if proj is not None else ""),
+             "tokens_per_s": total / float(proxy_ends[-1]), **summary(proxy_ends)}
+    # share of requests meeting both a first-token and a token-pace threshold (the pages give
+    # no thresholds: a grid of them)
+    ttft_px, pace_px = latencies(proxy_ends)
+    ok_pace = lambda b: np.isnan(pace_px) | (pace_px <= b)
+    proxy["sla_attainment"] = {f"ttft<={a}s,pace<={b}s": float(np.mean((ttft_px <= a) & ok_pace(b)))
+                               for a in (0.5, 1.0, 2.0) for b in (0.025, 0.05, 0.1)}
     result = {
         "metric": "serving-loop tokens/s (continuous SplitFuse passes, whole request stream)",
         "value": total / wall, "unit": "tokens/s", "n_gpus": 1, "steps": st.passes,
@@ -395,19 +451,10 @@ def serving_main(args):
                    "token_budget": sw.budget, "q_heads": v.num_q_heads,
                    "kv_heads": v.num_kv_heads, "head_dim": v.head_dim,
                    "block_size": v.block_size, "pool_blocks": v.num_blocks,
-                   "prompt_mean": 2600, "output_mean": 60, "cv": 0.3},
-        "serving": {"passes": st.passes, "tokens": total,
-                    "full_budget_passes": int((T == sw.budget).sum()),
-                    "mean_T": float(T.mean()), "mean_S": float(np.mean(st.seqs)),
-                    "gpu_s": float(app.sum() + att.sum()), "wall_s": wall,
-                    "gpu_only_tokens_per_s": total / float(app.sum() + att.sum()),
-                    "attention_us_mean": float(att.mean() * 1e6),
-                    "kv_append_us_mean": float(app.mean() * 1e6),
-                    "ttft_passes_mean": float(np.mean(ttft_p)),
-                    "ttft_ms_mean": float(np.mean(ttft_s) * 1e3),
-                    "ttft_ms_p95": float(np.percentile(ttft_s, 95) * 1e3),
-                    "token_pace_ms_mean": float(np.mean(pace_s) * 1e3),
-                    "token_pace_ms_p95": float(np.percentile(pace_s, 95) * 1e3)},
+                   "prompt_mean": 2600, "output_mean": 60, "cv": 0.3,
+                   "projections": proj is not None},
+        "serving": serving,
+        "latency_proxy": proxy,
         "roofline": None,
         "cpu_baseline": None,
     }

@@ -216,6 +216,21 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---- diagnostics -------------------------------------------------------------------- */
+/* ---- dense projections either side of attention ------------------------------------ */
+
+/* The layer ops next to the pass (paper card "Key points": FastGen's kernels come from
+ * FlashAttention and FasterTransformer): the QKV projection whose K and V rows feed
+ * fg_kv_append and whose Q rows feed fg_ragged_attention, and the output projection of the
+ * attention rows.  y[T][N] = x[T][K] . w[N][K]^T (w in the [out][in] layout of a linear
+ * layer), all three bf16, device memory, row-major and dense; fp32 accumulation, one rounding
+ * to bf16 (nearest even) per output.  A plain GEMM, run by hipBLASLt.  The first call on a
+ * device creates its hipBLASLt handle and a 32 MiB workspace (kept until the process ends);
+ * the first call for a (T, K, N) also picks the algorithm.  Calls on one device serialise on a
+ * lock.  Errors: FG_E_ARG (null pointer, T < 0, K or N < 1), FG_E_UNSUPPORTED (no algorithm),
+ * FG_E_HIP (a hipBLASLt or HIP error).  T = 0 does nothing. */
+fg_status fg_linear_bf16(const void *x, const void *w, void *y, int32_t T, int32_t K, int32_t N,
+                         void *stream);
+
 const char *fg_status_string(fg_status status);
 const char *fg_last_error(void);
 

@@ -25,6 +25,13 @@ What it computes, in plain numpy float64 (slow and obviously correct):
   its sequence's whole cached history, gathered through the block table
   (paper card "Key points" and "References": FlashAttention, an exact
   attention, is the kernel family used).
+* ``serving``   — the multi-pass loop around the pass: closed-loop clients,
+  continuous batching, retirement of finished requests and reuse of their
+  blocks (paper card "Key points": continuous batching, blocked KV cache, 1 to
+  32 clients and 512 requests).
+* ``linear``    — the dense projections either side of attention, y = x . w^T
+  (paper card "Key points": the surrounding kernels come from
+  FasterTransformer).
 
 Parity pins live in ``tests/test_oracle_*.py`` (brute force, closed forms,
 block-permutation and chunking invariants, hand-derived fixtures under
@@ -34,8 +41,10 @@ from .bf16 import bf16_bits_to_f64
 from .compose import FreeList, OracleBatch, SeqState, splitfuse_compose, commit_pass
 from .append import kv_append
 from .attention import ragged_attention
+from .linear import linear
+from .serving import serve
 
 __all__ = [
     "bf16_bits_to_f64", "FreeList", "OracleBatch", "SeqState", "splitfuse_compose",
-    "commit_pass", "kv_append", "ragged_attention",
+    "commit_pass", "kv_append", "ragged_attention", "linear", "serve",
 ]

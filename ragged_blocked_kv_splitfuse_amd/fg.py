@@ -25,7 +25,7 @@ EXPORTS = [
     "fg_blocked_cache_init", "fg_blocked_cache_destroy", "fg_blocked_cache_num_free",
     "fg_blocked_cache_free_ids", "fg_blocked_cache_release", "fg_splitfuse_compose",
     "fg_splitfuse_commit", "fg_splitfuse_retire", "fg_validate_batch", "fg_kv_append", "fg_attention_plan",
-    "fg_ragged_attention", "fg_status_string", "fg_last_error",
+    "fg_ragged_attention", "fg_linear_bf16", "fg_status_string", "fg_last_error",
 ]
 
 i32p = ctypes.POINTER(ctypes.c_int32)
@@ -111,6 +111,7 @@ def _declare(L):
         "fg_ragged_attention": ([vp, ctypes.POINTER(FgRaggedBatch), ctypes.POINTER(FgPlanInfo),
                                  vp, vp, ctypes.c_int32, ctypes.c_float, vp, vp,
                                  ctypes.c_size_t, vp], st),
+        "fg_linear_bf16": ([vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp], st),
         "fg_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "fg_last_error": ([], ctypes.c_char_p),
     }
@@ -304,3 +305,8 @@ def fg_ragged_attention(handle, dev: FgRaggedBatch, info: FgPlanInfo, work_dev_p
                                      work_dev_ptr or None, q_ptr,
                                      int(num_q_heads), float(scale), out_ptr, workspace_ptr,
                                      int(workspace_bytes), stream))
+
+
+def fg_linear_bf16(x_ptr, w_ptr, y_ptr, T, K, N, stream):
+    """y[T][N] = x[T][K] . w[N][K]^T in bf16 (device pointers)."""
+    _check(lib().fg_linear_bf16(x_ptr, w_ptr, y_ptr, int(T), int(K), int(N), stream))

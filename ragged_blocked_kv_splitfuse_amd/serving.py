@@ -135,17 +135,54 @@ class ServingLoop:
         return st
 
 
+class Projections:
+    """The dense projections of one attention layer (``fg_linear_bf16``): Q, K and V from the
+    pass's hidden rows x [T][hidden] (separate weights, so each lands in the dense layout the
+    pass reads), and the output projection of attention's rows."""
+
+    def __init__(self, wq, wk, wv, wo, budget: int, stream=None):
+        import torch
+        self.wq, self.wk, self.wv, self.wo = wq, wk, wv, wo
+        self.hidden = int(wq.shape[1])
+        self.stream = stream
+        dev, dt = wq.device, wq.dtype
+        mk = lambda n: torch.empty((max(int(budget), 1), int(n)), dtype=dt, device=dev)
+        self.q, self.k, self.v = mk(wq.shape[0]), mk(wk.shape[0]), mk(wv.shape[0])
+        self.y = mk(wo.shape[0])
+
+    def _lin(self, x, w, y, T):
+        from .runtime import stream_handle
+        fg.fg_linear_bf16(x.data_ptr(), w.data_ptr(), y.data_ptr(), T, int(w.shape[1]),
+                          int(w.shape[0]), stream_handle(self.stream))
+
+    def qkv(self, x, T):
+        for w, y in ((self.wq, self.q), (self.wk, self.k), (self.wv, self.v)):
+            self._lin(x, w, y, T)
+        return self.q[:T], self.k[:T], self.v[:T]
+
+    def output(self, o, T):
+        self._lin(o, self.wo, self.y, T)
+        return self.y[:T]
+
+    def flops(self, T) -> int:
+        return 2 * T * self.hidden * sum(int(w.shape[0]) for w in (self.wq, self.wk, self.wv)) \
+            + 2 * T * int(self.wo.shape[1]) * int(self.wo.shape[0])
+
+
 class DevicePass:
     """Device work of one serving pass: plan, descriptor upload, kv_append, attention.
 
     ``cache``: an object with ``handle`` (the library's cache handle) and ``head_dim``;
     ``rows(batch, running)`` returns the pass's (q, k_new, v_new) device tensors in batch
-    order; ``check(p, batch, out)`` (optional) sees every pass's output.  With ``timing``,
-    three events per pass (before kv_append, between the two kernels, after attention) are
-    kept in ``marks``."""
+    order -- or, with ``proj`` (a ``Projections``), its hidden rows x, from which the pass
+    computes q, k and v, and after attention the output projection.  ``check(p, batch, out)``
+    (optional) sees every pass's attention output.  With ``timing``, five events per pass are
+    kept in ``marks``: before the QKV projection, before kv_append, before attention, after
+    attention, after the output projection (without ``proj`` the first two and the last two
+    coincide)."""
 
     def __init__(self, cache, num_q_heads: int, scale: float, rows, num_cus: int,
-                 check=None, stream=None, timing: bool = False):
+                 check=None, stream=None, timing: bool = False, proj=None):
         from .runtime import DeviceDescriptors, Workspace
         self.cache, self.hq, self.scale = cache, int(num_q_heads), float(scale)
         self.rows, self.check, self.num_cus = rows, check, int(num_cus)
@@ -155,6 +192,7 @@ class DevicePass:
         self.p = 0
         self.out = None
         self.timing, self.marks = bool(timing), []
+        self.proj = proj
 
     def __call__(self, hb, running):
         import torch
@@ -164,17 +202,23 @@ class DevicePass:
         if work is not None and work.size > self.work.size:
             self.work = np.zeros(2 * work.size, np.int32)
         c = self.desc.upload(hb, work if info.num_work else None, self.stream)
-        q, kn, vn = self.rows(hb, running)
+        T = hb.num_tokens
         s = stream_handle(self.stream)
         ev = None
         if self.timing:
             st = self.stream or torch.cuda.current_stream()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
             ev[0].record(st)
-        fg.fg_kv_append(self.cache.handle, c, kn.data_ptr(), vn.data_ptr(), s)
+        if self.proj is not None:
+            x = self.rows(hb, running)
+            q, kn, vn = self.proj.qkv(x, T)
+        else:
+            q, kn, vn = self.rows(hb, running)
         if ev:
             ev[1].record(st)
-        T = hb.num_tokens
+        fg.fg_kv_append(self.cache.handle, c, kn.data_ptr(), vn.data_ptr(), s)
+        if ev:
+            ev[2].record(st)
         if self.out is None or self.out.shape[0] < T:
             self.out = torch.empty((max(T, 1), self.hq, self.cache.head_dim), dtype=q.dtype,
                                    device=q.device)
@@ -183,7 +227,11 @@ class DevicePass:
         fg.fg_ragged_attention(self.cache.handle, c, info, self.desc.work_ptr, q.data_ptr(),
                                self.hq, self.scale, out.data_ptr(), wp, wb, s)
         if ev:
-            ev[2].record(st)
+            ev[3].record(st)
+        if self.proj is not None:
+            self.proj.output(out.view(T, -1), T)
+        if ev:
+            ev[4].record(st)
             self.marks.append(ev)
         if self.check is not None:
             self.check(self.p, hb, out)
