@@ -33,7 +33,7 @@ What it computes, in plain numpy float64 (slow and obviously correct):
   (paper card "Key points": the surrounding kernels come from
   FasterTransformer).
 
-Parity pins live in ``tests/test_oracle_*.py`` (brute force, closed forms,
+Parity pins live in ``tests/test_oracle_*.py`` and ``tests/test_serving.py`` (brute force, closed forms,
 block-permutation and chunking invariants, hand-derived fixtures under
 ``tests/golden/``).  No oracle function is "parity unpinned".
 """
