@@ -59,6 +59,11 @@ typedef enum fg_dtype { FG_F32 = 0, FG_BF16 = 1 } fg_dtype;
 
 /* Number of int32 per work item in the work list produced by fg_attention_plan. */
 #define FG_ITEM_INTS 12
+/* Query rows (tokens x query heads per KV head) of one attention work item: up to
+ * FG_STREAM_ROWS rows are a stream item, longer row sets are cut into tile items of up to
+ * FG_TILE_ROWS rows; a split item's workspace partial holds that many rows. */
+#define FG_STREAM_ROWS 16
+#define FG_TILE_ROWS 128
 
 typedef struct fg_cache fg_cache; /* opaque, host-side */
 

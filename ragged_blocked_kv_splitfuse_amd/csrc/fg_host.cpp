@@ -365,12 +365,11 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
   }
   double total = 0;
   for (auto &it : base) total += (double)it.cost * Hkv;
-  // aim for about two records per compute unit: one full wave of resident workgroups; finer
-  // splits cost partial-result traffic and merge work.  A shape is cut into round(cost /
-  // target) pieces (not the ceiling): equal shapes slightly above a multiple of the target
-  // would otherwise spill a few records into a second, nearly empty wave.
-  const double target = total / (2.0 * num_cus);
-  const int32_t min_tiles = 4;  // a split covers at least 4 key tiles (256 keys)
+  // aim for one full wave of resident workgroups (WG_PER_CU per compute unit); finer splits
+  // cost partial-result traffic and merge work.  A shape is cut into round(cost / target)
+  // pieces (not the ceiling): equal shapes slightly above a multiple of the target would
+  // otherwise spill a few records into a second, nearly empty wave.
+  const double target = total / ((double)WG_PER_CU * num_cus);
 
   std::vector<PlanItem> &items = cache->plan_items;  // one entry per shape and split
   items.clear();
@@ -384,6 +383,8 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
     // cheap to write and merge.  Tile splits cost a 128-row partial and a Q reload each.
     const double tg = it.mode == MODE_STREAM ? target / 8 : target;
     if (tg > 0 && it.cost > tg) nsplit = (int32_t)std::lround(it.cost / tg);
+    // a split covers at least 4 key tiles (256 keys), a stream split one per wave
+    const int32_t min_tiles = it.mode == MODE_STREAM ? std::max(4, WAVES_PER_WG) : 4;
     nsplit = std::max(1, std::min(nsplit, tiles / min_tiles));
     if (nsplit == 1) {
       items.push_back(it);

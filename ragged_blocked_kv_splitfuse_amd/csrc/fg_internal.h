@@ -52,8 +52,13 @@ enum ItemField {
 // of a workgroup take alternate key tiles and merge at the end.
 // MODE_TILE: up to TILE_ROWS query rows; all waves share every K/V tile staged in LDS.
 enum { MODE_STREAM = 0, MODE_TILE = 1 };
-constexpr int STREAM_ROWS = 16;
-constexpr int TILE_ROWS = 128;
+constexpr int STREAM_ROWS = FG_STREAM_ROWS;
+constexpr int TILE_ROWS = FG_TILE_ROWS;
+// A workgroup of the attention launch is WAVES_PER_WG waves; a tile record gives each wave 32
+// query rows, and WG_PER_CU workgroups are resident per compute unit (two waves per SIMD).
+constexpr int WAVES_PER_WG = TILE_ROWS / 32;
+constexpr int WG_PER_CU = 8 / WAVES_PER_WG;
+static_assert(WAVES_PER_WG == 4 || WAVES_PER_WG == 8, "4 or 8 waves per workgroup");
 constexpr int KEY_TILE = 64;
 
 constexpr int64_t slot_floats(int mode, int head_dim) {

@@ -39,8 +39,13 @@ namespace {
 
 constexpr int D = 128;          // head dim of the bf16 kernels
 constexpr int KT = KEY_TILE;    // keys per tile
-constexpr int NW = 4;           // waves per workgroup
+constexpr int NW = WAVES_PER_WG;  // waves per workgroup
 constexpr int NT = NW * 64;     // threads per workgroup
+// The LDS stage ring of tile records (also the stream records' merge space)
+constexpr int KS = 32;                     // keys per stage
+constexpr int NSTAGE = 4;                  // ring depth
+constexpr int STAGE_K = KS * D;            // u16 elements of the K part of a stage
+constexpr int STAGE_ELEMS = 2 * KS * D;    // K + V^T: 16 KiB
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float NEG_INF = -__builtin_inff();
 
@@ -255,11 +260,11 @@ __device__ __forceinline__ void online_softmax(f32x4 (&s)[2][2], bool need_mask,
   pf[1] = to_bf16x8(p[1]);
 }
 
-constexpr int MERGE_ROWS = NT / (D / 8);  // rows one merge workgroup covers (16)
+constexpr int MERGE_ROWS = NT / (D / 8);  // rows one merge workgroup covers
 
 // Combine: the merge record of a split group reads every split's (m, l, acc) partial in
 // split order (deterministic) and writes O.  Runs in its own launch after the main kernel.
-// Each workgroup merges one 16-row slice (blockIdx.y) of the group: one thread per (row,
+// Each workgroup merges one MERGE_ROWS-row slice (blockIdx.y) of the group: one thread per (row,
 // 8-feature chunk).
 __device__ void merge_splits(const Params &P, const Rec &R) {
   const int64_t slot = slot_floats(R.mode, D);
@@ -413,11 +418,11 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
 
-  // ---- merge the four waves through LDS ------------------------------------------------
-  // per-wave O^T dumps: wave w uses the K half of stage buffer w (8 KiB = 16 rows x 128);
-  // a select chain keeps every LDS address tied to a fixed array
-  float *so_w = reinterpret_cast<float *>(S.k(w));
-  float *sm = reinterpret_cast<float *>(S.v(0));               // [NW][16]
+  // ---- merge the waves through LDS ---------------------------------------------------
+  // per-wave O^T dumps: wave w uses the w-th 8 KiB half-buffer of the ring (16 rows x 128
+  // floats); the running maxima and sums go to the block-id array
+  float *so_w = reinterpret_cast<float *>(S.base + w * STAGE_K);
+  float *sm = reinterpret_cast<float *>(S.ids);                // [NW][16]
   float *sl = sm + NW * STREAM_ROWS;                           // [NW][16]
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
@@ -438,7 +443,7 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
     const float m = sm[ww * STREAM_ROWS + row];
     const float f = (m == NEG_INF) ? 0.f : fast_exp2(m - M);
     Lsum += sl[ww * STREAM_ROWS + row] * f;
-    const float *src = reinterpret_cast<const float *>(S.k(ww)) + row * D + chunk * 8;
+    const float *src = reinterpret_cast<const float *>(S.base + ww * STAGE_K) + row * D + chunk * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] += src[i] * f;
   }
@@ -472,11 +477,8 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
 // row's softmax state lives in two lanes (l, l^32), and all 64 accumulators of a lane belong
 // to one row, one scale factor.
 // ---------------------------------------------------------------------------------------
-constexpr int KS = 32;                     // keys per stage
-constexpr int NSTAGE = 4;                  // ring depth
-constexpr int STAGE_K = KS * D;            // u16 elements of the K part of a stage
-constexpr int STAGE_ELEMS = 2 * KS * D;    // K + V^T: 16 KiB
 static_assert(STREAM_ROWS * D * 4 <= STAGE_K * 2, "a wave's stream dump must fit a K array");
+static_assert(NW * STAGE_K <= NSTAGE * STAGE_ELEMS, "every wave's stream dump must fit the ring");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
@@ -498,6 +500,7 @@ __device__ __forceinline__ int key_perm32(int m) {
 // V^T [128][32 keys].  Buffers are addressed as base + constant offset, so one set of per-lane
 // address registers serves every buffer.
 constexpr int MAX_IDS = 256;  // block ids of a tile record staged in LDS
+static_assert(2 * NW * STREAM_ROWS <= MAX_IDS, "stream merge maxima and sums must fit");
 
 struct Lds {
   u16 *base;
@@ -535,28 +538,34 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// wait until at most n of this wave's LDS-DMA loads are outstanding (n in {0, 4, .., 16})
+// wait until at most n of this wave's LDS-DMA loads are outstanding (n even, 0 .. 16; an odd
+// or larger n waits for n rounded down)
 __device__ __forceinline__ void wait_dma(int n) {
   // s_waitcnt encoding (gfx9): vmcnt = bits 3:0 (+15:14), expcnt 6:4, lgkmcnt 11:8
   if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt 16: bits 15:14 = 1, 3:0 = 0
+  else if (n >= 14) __builtin_amdgcn_s_waitcnt(0x0F70 | 14);
   else if (n >= 12) __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
+  else if (n >= 10) __builtin_amdgcn_s_waitcnt(0x0F70 | 10);
   else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+  else if (n >= 6) __builtin_amdgcn_s_waitcnt(0x0F70 | 6);
   else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+  else if (n >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 // Per-lane parts of the four LDS-DMA source addresses of a stage (bytes from the stage's
 // first key in its block), constant over a record when a stage lies inside one block.
+constexpr int RPW = 8 / NW;  // 1 KiB regions of each stage half a wave fetches
 struct DmaOffsets {
-  uint32_t k[2], v[2];
+  uint32_t k[RPW], v[RPW];
 };
 
 __device__ __forceinline__ DmaOffsets dma_offsets(int bs) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   DmaOffsets o;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int reg = 2 * w + p;
+  for (int p = 0; p < RPW; ++p) {
+    const int reg = RPW * w + p;
     // K: region `reg` holds key rows 4*reg .. 4*reg+3; lane -> (key row, 16-byte slot)
     const int keyl = 4 * reg + (lane >> 4), ch = (lane & 15) ^ swz_k32(keyl);
     o.k[p] = (uint32_t)(keyl * D + 8 * ch) * 2u;
@@ -576,21 +585,21 @@ __device__ __forceinline__ void issue_stage(const Params &P, const Rec &R, const
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int bs_mask = P.bs - 1;
   const size_t head_stride = (size_t)P.bs * D;
-  const uint32_t kl = lds_addr_of(buf) + 2048u * w, vl = lds_addr_of(vbuf) + 2048u * w;
+  const uint32_t kl = lds_addr_of(buf) + 1024u * RPW * w, vl = lds_addr_of(vbuf) + 1024u * RPW * w;
   if (BSC >= 1) {
     // a 32-key stage lies in one block: uniform base + per-lane offset
     const size_t hb = ((size_t)blk * P.Hkv + R.h) * head_stride;
     const char *kb = reinterpret_cast<const char *>(P.k_pool + hb + (size_t)(k0 & bs_mask) * D);
     const char *vb = reinterpret_cast<const char *>(P.v_pool + hb + (k0 & bs_mask));
 #pragma unroll
-    for (int p = 0; p < 2; ++p) dma16(reinterpret_cast<const u16 *>(kb + o.k[p]), kl + 1024u * p);
+    for (int p = 0; p < RPW; ++p) dma16(reinterpret_cast<const u16 *>(kb + o.k[p]), kl + 1024u * p);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) dma16(reinterpret_cast<const u16 *>(vb + o.v[p]), vl + 1024u * p);
+    for (int p = 0; p < RPW; ++p) dma16(reinterpret_cast<const u16 *>(vb + o.v[p]), vl + 1024u * p);
     return;
   }
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int reg = 2 * w + p;
+  for (int p = 0; p < RPW; ++p) {
+    const int reg = RPW * w + p;
     const int keyl = 4 * reg + (lane >> 4), ch = (lane & 15) ^ swz_k32(keyl);
     const int key = min(k0 + keyl, L - 1);
     const int blk = clamp_block(bt[key >> P.bs_log2], P.num_blocks);
@@ -598,8 +607,8 @@ __device__ __forceinline__ void issue_stage(const Params &P, const Rec &R, const
           kl + 1024u * p);
   }
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int reg = 2 * w + p;
+  for (int p = 0; p < RPW; ++p) {
+    const int reg = RPW * w + p;
     const int d = 16 * reg + (lane >> 2), kc = (lane & 3) ^ swz_v32(d);
     const int key0 = min(k0 + 8 * kc, (L - 1) & ~7);
     const int blk = clamp_block(bt[key0 >> P.bs_log2], P.num_blocks);
@@ -768,7 +777,7 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
       const int i = base + u;
       if (i >= nst) break;
       const int k0 = (s_begin + i) * KS;
-      wait_dma(4 * min(NSTAGE - 2, nst - 1 - i));  // this wave's loads of stage i landed
+      wait_dma(2 * RPW * min(NSTAGE - 2, nst - 1 - i));  // this wave's loads of stage i landed
       stage_barrier();                              // ... and every other wave's
       if (i + NSTAGE - 1 < nst) {                   // refill the buffer stage i-1 used
         issue_stage<BSC>(P, R, bt, L, (s_begin + i + NSTAGE - 1) * KS,
@@ -846,7 +855,7 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
 // tile records (chunk rows, MFMA-bound); the branch is uniform per workgroup.
 // BSC: 0 = blocks of < 32 keys, 1 = blocks of 32 keys, 2 = blocks of >= 64 keys.
 template <int BSC>
-__global__ __launch_bounds__(NT, 2) void attention_bf16_kernel(Params P) {
+__global__ __launch_bounds__(NT, WG_PER_CU) void attention_bf16_kernel(Params P) {
   __shared__ __attribute__((aligned(16))) u16 ring[NSTAGE * STAGE_ELEMS];
   __shared__ int blk_ids[MAX_IDS];
   const Rec R = load_rec(P, blockIdx.x);

@@ -318,7 +318,7 @@ def decode_plan(info, work, hkv, head_dim=128):
     ni, IW = info.num_items, fg.FG_ITEM_INTS
     assert info.work_ints == len(work) == ni * IW + info.num_work
     items = work[:ni * IW].reshape(ni, IW)
-    slot = {0: 16 * (head_dim + 2), 1: 128 * (head_dim + 2)}
+    slot = {0: fg.FG_STREAM_ROWS * (head_dim + 2), 1: fg.FG_TILE_ROWS * (head_dim + 2)}
     recs = np.full((info.num_work, 11), -1, np.int64)
     for r, code in enumerate(work[ni * IW:]):
         code = int(code)
@@ -340,7 +340,7 @@ def check_plan(hb, info, work, hq, hkv, head_dim=128):
     work = decode_plan(info, work, hkv, head_dim)
     assert info.num_work == len(work) and 0 <= info.num_groups < max(info.num_work, 1)
     main, merges = work[:info.num_work - info.num_groups], work[info.num_work - info.num_groups:]
-    slot = {0: 16 * (head_dim + 2), 1: 128 * (head_dim + 2)}
+    slot = {0: fg.FG_STREAM_ROWS * (head_dim + 2), 1: fg.FG_TILE_ROWS * (head_dim + 2)}
     groups = {}
     cover = {}
     # the main list is laid out for the 8 XCDs (record i runs on XCD i % 8); lists that run
@@ -360,7 +360,7 @@ def check_plan(hb, info, work, hq, hkv, head_dim=128):
             continue
         s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff = (int(x) for x in rec)
         assert 0 <= s < S and 0 <= h < hkv and nt >= 1 and sp >= 0
-        assert mode == (0 if nt * G <= 16 else 1) and nt * G <= 128
+        assert mode == (0 if nt * G <= fg.FG_STREAM_ROWS else 1) and nt * G <= fg.FG_TILE_ROWS
         c, n = int(hb.context_len[s]), int(hb.n_query[s])
         assert 0 <= t0 and t0 + nt <= n
         assert klo % 64 == 0 and klo < khi <= c + t0 + nt
