@@ -961,20 +961,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   constexpr int ROWP = HD + 4 / sizeof(T);       // LDS row padded by one dword
   __shared__ int dblk[APPEND_TOKENS], dslot[APPEND_TOKENS];
   __shared__ T vt[APPEND_TOKENS * ROWP];
-  constexpr int PER_THREAD = APPEND_TOKENS * CPR / 256;  // 16-byte chunks of K (and V) each
   const int t0 = blockIdx.x * APPEND_TOKENS, h = blockIdx.y, tid = threadIdx.x;
-  const size_t row_in = (size_t)Hkv * HD;  // elements per token in k_new / v_new
-  // The new rows first: their loads do not depend on where they go, so they overlap the
-  // destination lookup below instead of following it.
-  uint4 kr[PER_THREAD], vr[PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < PER_THREAD; ++i) {
-    const int q = tid + 256 * i, tok = q / CPR, c = q % CPR;
-    const bool in = t0 + tok < num_tokens;
-    const size_t off = (size_t)(in ? t0 + tok : 0) * row_in + h * HD + c * VEC;
-    kr[i] = *reinterpret_cast<const uint4 *>(k_new + off);
-    vr[i] = *reinterpret_cast<const uint4 *>(v_new + off);
-  }
   if (tid < APPEND_TOKENS) {
     const int t = t0 + tid;
     int blk = -1, slot = 0;
@@ -994,25 +981,27 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     dblk[tid] = blk;
     dslot[tid] = slot;
   }
-  // V rows to LDS (token-major), for the feature-major stores
-#pragma unroll
-  for (int i = 0; i < PER_THREAD; ++i) {
-    const int q = tid + 256 * i, tok = q / CPR, c = q % CPR;
-    uint32_t *dst = reinterpret_cast<uint32_t *>(vt + tok * ROWP + c * VEC);
-    dst[0] = vr[i].x;
-    dst[1] = vr[i].y;
-    dst[2] = vr[i].z;
-    dst[3] = vr[i].w;
-  }
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < PER_THREAD; ++i) {
-    const int q = tid + 256 * i, tok = q / CPR, c = q % CPR;
+  const size_t row_in = (size_t)Hkv * HD;  // elements per token in k_new / v_new
+  for (int q = tid; q < APPEND_TOKENS * CPR; q += blockDim.x) {
+    const int tok = q / CPR, c = q % CPR;
     const int blk = dblk[tok];
     if (blk < 0) continue;
+    const uint4 v = *reinterpret_cast<const uint4 *>(k_new + (t0 + tok) * row_in + h * HD + c * VEC);
     *reinterpret_cast<uint4 *>(k_pool + (((size_t)blk * Hkv + h) * bs + dslot[tok]) * HD +
-                               c * VEC) = kr[i];
+                               c * VEC) = v;
   }
+  for (int q = tid; q < APPEND_TOKENS * CPR; q += blockDim.x) {
+    const int tok = q / CPR, c = q % CPR;
+    if (t0 + tok >= num_tokens) continue;
+    const uint4 v = *reinterpret_cast<const uint4 *>(v_new + (t0 + tok) * row_in + h * HD + c * VEC);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(vt + tok * ROWP + c * VEC);
+    dst[0] = v.x;
+    dst[1] = v.y;
+    dst[2] = v.z;
+    dst[3] = v.w;
+  }
+  __syncthreads();
   const int tok = tid % APPEND_TOKENS;
   const int blk = dblk[tok];
   if (blk < 0) return;
