@@ -558,6 +558,11 @@ __device__ __forceinline__ void wait_dma(int n) {
 constexpr int RPW = 8 / NW;  // 1 KiB regions of each stage half a wave fetches
 struct DmaOffsets {
   uint32_t k[RPW], v[RPW];
+  // the record's KV head in block 0 of each pool, and the bytes from one block to the next
+  // (wave-uniform, so a stage's address is one scalar multiply-add away)
+  const char *kh0, *vh0;
+  uint64_t blk_bytes;
+  uint32_t wave_lds;  // byte offset of this wave's regions inside a stage half
 };
 
 __device__ __forceinline__ DmaOffsets dma_offsets(int bs) {
@@ -585,12 +590,13 @@ __device__ __forceinline__ void issue_stage(const Params &P, const Rec &R, const
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int bs_mask = P.bs - 1;
   const size_t head_stride = (size_t)P.bs * D;
-  const uint32_t kl = lds_addr_of(buf) + 1024u * RPW * w, vl = lds_addr_of(vbuf) + 1024u * RPW * w;
+  const uint32_t kl = lds_addr_of(buf) + o.wave_lds, vl = lds_addr_of(vbuf) + o.wave_lds;
   if (BSC >= 1) {
     // a 32-key stage lies in one block: uniform base + per-lane offset
-    const size_t hb = ((size_t)blk * P.Hkv + R.h) * head_stride;
-    const char *kb = reinterpret_cast<const char *>(P.k_pool + hb + (size_t)(k0 & bs_mask) * D);
-    const char *vb = reinterpret_cast<const char *>(P.v_pool + hb + (k0 & bs_mask));
+    const uint64_t hb = (uint64_t)(uint32_t)blk * o.blk_bytes;
+    const uint32_t key_in_blk = (uint32_t)(k0 & bs_mask);
+    const char *kb = o.kh0 + hb + key_in_blk * (uint32_t)(D * 2);
+    const char *vb = o.vh0 + hb + key_in_blk * 2u;
 #pragma unroll
     for (int p = 0; p < RPW; ++p) dma16(reinterpret_cast<const u16 *>(kb + o.k[p]), kl + 1024u * p);
 #pragma unroll
@@ -706,7 +712,14 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
   const int vswz = swz_v32(n);                     // swz_v32(32*dt + n) == swz_v32(n)
 
   const int s_begin = R.klo / KS, s_end = (R.khi + KS - 1) / KS, nst = s_end - s_begin;
-  const DmaOffsets doff = dma_offsets(P.bs);
+  DmaOffsets doff = dma_offsets(P.bs);
+  {
+    const uint64_t head_bytes = (uint64_t)P.bs * D * 2;
+    doff.kh0 = reinterpret_cast<const char *>(P.k_pool) + (uint64_t)R.h * head_bytes;
+    doff.vh0 = reinterpret_cast<const char *>(P.v_pool) + (uint64_t)R.h * head_bytes;
+    doff.blk_bytes = (uint64_t)P.Hkv * head_bytes;
+    doff.wave_lds = __builtin_amdgcn_readfirstlane(1024u * RPW * (threadIdx.x >> 6));
+  }
 
   // Keys at or past khi in the last stage may hold stale bits: zero their V so they cannot
   // reach O.  Called once that stage has landed for every wave.
@@ -771,7 +784,48 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
     }
   }
 
-  for (int base = 0; base < nst; base += NSTAGE) {
+  // Steady state: the stages before the last NSTAGE and before any masked key (the record's
+  // first row sees every key of them) need no mask, no tail zeroing, no refill or wait
+  // bounds and no per-wave skip.  They run in a loop without those branches, NSTAGE at a
+  // time; the general loop below takes the rest.
+  int steady = 0;
+  if (BSC >= 1 && ids_in_lds && rows > 32 * (NW - 1)) {
+    const int unmasked = (c + R.tok0 + 1) / KS - s_begin;  // stages with k0 + KS - 1 <= first limit
+    steady = max(0, min(unmasked, nst - NSTAGE));
+    steady -= steady % NSTAGE;
+  }
+  for (int base = 0; base < steady; base += NSTAGE) {
+#pragma unroll
+    for (int u = 0; u < NSTAGE; ++u) {
+      const int i = base + u;
+      wait_dma(2 * RPW * (NSTAGE - 2));
+      stage_barrier();
+      issue_stage<BSC>(P, R, bt, L, (s_begin + i + NSTAGE - 1) * KS,
+                       __builtin_amdgcn_readfirstlane(blk_next), doff,
+                       S.k((u + NSTAGE - 1) % NSTAGE), S.v((u + NSTAGE - 1) % NSTAGE));
+      blk_next = S.ids[(((s_begin + i + NSTAGE) * KS) >> P.bs_log2) - b_first];
+      scores(S.k(u), sc);
+      const u16 *Vl = S.v(u);
+      bf16x8 vf[D / 32][2];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          vf[dt][h] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+              Vl + (32 * dt + n) * KS + 8 * ((2 * h + g) ^ vswz)));
+      bf16x8 pf[2];
+      if (!softmax_t32_fast(sc, P.sl2, m_run, l_run, pf)) {
+        scores(S.k(u), sc);
+        online_softmax_t32(sc, P.sl2, m_run, l_run, acc, pf);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        acc[dt] = mfma32_bf16(vf[dt][0], pf[0], acc[dt]);
+        acc[dt] = mfma32_bf16(vf[dt][1], pf[1], acc[dt]);
+      }
+    }
+  }
+  for (int base = steady; base < nst; base += NSTAGE) {
 #pragma unroll
     for (int u = 0; u < NSTAGE; ++u) {   // unrolled so every stage buffer is a fixed array
       const int i = base + u;
