@@ -63,7 +63,7 @@ typedef enum fg_dtype { FG_F32 = 0, FG_BF16 = 1 } fg_dtype;
  * FG_STREAM_ROWS rows are a stream item, longer row sets are cut into tile items of up to
  * FG_TILE_ROWS rows; a split item's workspace partial holds that many rows. */
 #define FG_STREAM_ROWS 16
-#define FG_TILE_ROWS 128
+#define FG_TILE_ROWS 256
 
 typedef struct fg_cache fg_cache; /* opaque, host-side */
 

@@ -17,7 +17,7 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfg.so")
 FG_ITEM_INTS = 12
 FG_STREAM_ROWS = 16   # query rows of a stream work item (include/fg.h)
-FG_TILE_ROWS = 128    # query rows of a tile work item
+FG_TILE_ROWS = 256    # query rows of a tile work item
 
 FG_OK, FG_E_ARG, FG_E_DESC, FG_E_NO_BLOCKS, FG_E_UNSUPPORTED, FG_E_HIP, FG_E_WORKSPACE = range(7)
 FG_F32, FG_BF16 = 0, 1
