@@ -44,10 +44,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 
 def kernel_source_hash():
     """Hash of the sources that decide the kernels' work: the device code, the shared internal
-    header and the public header (item row sizes)."""
+    header, the planner and the public header (item row sizes)."""
     h = hashlib.sha256()
     for f in (("ragged_blocked_kv_splitfuse_amd", "csrc", "fg_kernels.hip"),
               ("ragged_blocked_kv_splitfuse_amd", "csrc", "fg_internal.h"),
+              ("ragged_blocked_kv_splitfuse_amd", "csrc", "fg_host.cpp"),
               ("include", "fg.h")):
         with open(os.path.join(ROOT, *f), "rb") as fh:
             h.update(fh.read())

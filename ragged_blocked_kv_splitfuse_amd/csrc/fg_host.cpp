@@ -378,10 +378,13 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *b,
   for (auto &it : base) {
     const int32_t tiles = (it.khi + KEY_TILE - 1) / KEY_TILE;
     int32_t nsplit = 1;
-    // Stream records are cut 8x finer: one streams at a fixed per-workgroup rate however idle
-    // the chip is, so a long one becomes the pass's tail, while its split partial (16 rows) is
-    // cheap to write and merge.  Tile splits cost a 128-row partial and a Q reload each.
-    const double tg = it.mode == MODE_STREAM ? target / 8 : target;
+    // Stream records are cut 2x finer: one streams at a fixed per-workgroup rate however idle
+    // the chip is, so a long one can become the pass's tail, while its split partial (16 rows)
+    // is cheap to write and merge.  Tile splits cost a full-tile partial and a Q reload each.
+    // (With four-wave workgroups, two per CU, 8x finer stream splits paid; with one
+    // eight-wave workgroup per CU they only add merge work: on the LLaMA-2 mixed pass 2x
+    // leaves no split at all and the attention call takes 242 us instead of 256.)
+    const double tg = it.mode == MODE_STREAM ? target / 2 : target;
     if (tg > 0 && it.cost > tg) nsplit = (int32_t)std::lround(it.cost / tg);
     // a split covers at least 4 key tiles (256 keys), a stream split one per wave
     const int32_t min_tiles = it.mode == MODE_STREAM ? std::max(4, WAVES_PER_WG) : 4;
