@@ -48,8 +48,8 @@ enum ItemField {
   I_RES1 = 11
 };
 
-// MODE_STREAM: at most STREAM_ROWS query rows (decode tokens, short chunks); the four waves
-// of a workgroup take alternate key tiles and merge at the end.
+// MODE_STREAM: at most STREAM_ROWS query rows (decode tokens, short chunks); the waves of a
+// workgroup take key tiles in turn and merge at the end.
 // MODE_TILE: up to TILE_ROWS query rows; all waves share every K/V tile staged in LDS.
 enum { MODE_STREAM = 0, MODE_TILE = 1 };
 constexpr int STREAM_ROWS = FG_STREAM_ROWS;

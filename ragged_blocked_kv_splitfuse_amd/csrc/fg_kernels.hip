@@ -294,9 +294,9 @@ __device__ void merge_splits(const Params &P, const Rec &R) {
 }
 
 // ---------------------------------------------------------------------------------------
-// MODE_STREAM: <= 16 query rows.  Each wave streams its own key tiles (w, w+4, ...) straight
-// from HBM into MFMA operand registers (no LDS staging, no barriers), then the four waves
-// merge their running states through LDS.
+// MODE_STREAM: <= 16 query rows.  Each wave streams its own key tiles (w, w + NW, ...)
+// straight from HBM into MFMA operand registers (no LDS staging, no barriers), then the NW
+// waves merge their running states through LDS.
 // ---------------------------------------------------------------------------------------
 template <bool BIG, typename LdsT>
 __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
