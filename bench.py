@@ -264,7 +264,7 @@ def time_pass(S, steps, warmup):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
               "multi-GPU path; the pass shards by KV head or by sequence with no exchange "
               "inside it, see the design notes.", file=sys.stderr)
         sys.exit(2)

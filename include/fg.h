@@ -126,8 +126,10 @@ typedef struct fg_attention_plan_info {
  * are handed out (ids already owned by sequences must not be listed); free_ids may be NULL
  * with n_free = -1 to mean 0..num_blocks-1 in order.  The free list is a stack: released
  * ids are handed out next, the last released first.
- * Errors: FG_E_ARG (null out/cfg, sizes out of range, an id out of range or repeated),
- * FG_E_UNSUPPORTED (block_size/head_dim/dtype combination not implemented). */
+ * The kernels move 16 bytes per access, so both pools must be 16-byte aligned.
+ * Errors: FG_E_ARG (null out/cfg, sizes out of range, an id out of range or repeated, a pool
+ * not 16-byte aligned), FG_E_UNSUPPORTED (block_size/head_dim/dtype combination not
+ * implemented). */
 fg_status fg_blocked_cache_init(const fg_cache_config *cfg, void *k_pool, void *v_pool,
                                 const int32_t *free_ids, int32_t n_free, fg_cache **out);
 fg_status fg_blocked_cache_destroy(fg_cache *cache);
@@ -181,14 +183,15 @@ fg_status fg_validate_batch(const fg_cache *cache, const fg_ragged_batch *host);
 /* Appends the pass's new rows: new token i of sequence s (position context_len[s]+i) goes
  * to block block_table[s][pos / block_size], slot pos % block_size, of both pools.  A bit
  * copy; no other element of either pool is written.  `dev` arrays are device memory.
- * k_new, v_new: device [T][Hkv][D].  Errors: FG_E_ARG, FG_E_HIP. */
+ * k_new, v_new: device [T][Hkv][D], 16-byte aligned.  Errors: FG_E_ARG (null or unaligned
+ * pointers, negative sizes), FG_E_HIP. */
 fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const void *k_new,
                        const void *v_new, void *stream);
 
 /* Splits the attention of a host batch into work (host only).  Sequences with at most 16
  * query rows (rows = tokens x query heads per KV head) become key-streaming items, others
- * tiles of up to 128 rows; long key ranges are split so that about num_cus * 2 records'
- * worth of work exists.  A record is one item for one KV head.  The work list, info->
+ * tiles of up to FG_TILE_ROWS rows; long key ranges are split so that about one record per
+ * resident workgroup (one per compute unit) exists.  A record is one item for one KV head.  The work list, info->
  * work_ints int32 written to `work` (host), is
  *   items[num_items][FG_ITEM_INTS]   the items (layout private to this library), then
  *   codes[num_work]                  record r = codes[r]: item * Hkv + KV head, or -1 for a
@@ -213,7 +216,8 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *host,
  * launch runs every attention record (decode and chunk rows together); a second, small
  * launch merges split groups when the plan has any.  The workspace needs no initialisation
  * (its contents are scratch); calls sharing a workspace must be ordered on one stream.
- * Results are deterministic (no atomics; merges run in split order).
+ * Results are deterministic (no atomics; merges run in split order).  q, out and workspace
+ * must be 16-byte aligned.
  * Errors: FG_E_ARG, FG_E_UNSUPPORTED, FG_E_WORKSPACE, FG_E_HIP. */
 fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
                               const fg_attention_plan_info *plan, const int32_t *work_dev,

@@ -78,6 +78,8 @@ fg_status fg_blocked_cache_init(const fg_cache_config *cfg, void *k_pool, void *
   if (c.dtype == FG_F32 && c.head_dim != 64 && c.head_dim != 128)
     return fail(FG_E_UNSUPPORTED, "fp32 kernels implement head_dim 64 or 128 (got %d)",
                 c.head_dim);
+  if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
+    return fail(FG_E_ARG, "pools must be 16-byte aligned (k_pool %p, v_pool %p)", k_pool, v_pool);
   std::vector<int32_t> ids;
   if (n_free < 0) {
     if (free_ids) return fail(FG_E_ARG, "n_free < 0 requires free_ids == NULL");

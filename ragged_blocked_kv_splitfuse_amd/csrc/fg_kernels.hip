@@ -1081,6 +1081,8 @@ fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const 
     return fail(FG_E_ARG, "descriptor arrays are null");
   if (!k_new || !v_new || !cache->k_pool || !cache->v_pool)
     return fail(FG_E_ARG, "k_new, v_new and both pools must be device pointers");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(FG_E_ARG, "k_new and v_new must be 16-byte aligned");
   const fg_cache_config &c = cache->cfg;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid((dev->num_tokens + APPEND_TOKENS - 1) / APPEND_TOKENS, c.num_kv_heads);
@@ -1120,6 +1122,9 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
     return fail(FG_E_ARG, "descriptor arrays are null");
   if (!q || !out || !cache->k_pool || !cache->v_pool)
     return fail(FG_E_ARG, "q, out and both pools must be device pointers");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) |
+       reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return fail(FG_E_ARG, "q, out and workspace must be 16-byte aligned");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (c.dtype == FG_F32) {
     const dim3 grid((unsigned)dev->num_tokens * num_q_heads), block(64);

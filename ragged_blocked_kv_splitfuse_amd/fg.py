@@ -89,7 +89,7 @@ def load(path):
 
 
 def _declare(L):
-    """Set argument and return types of the entry points this build exports.
+    """Set argument and return types of the entry points the loaded library exports.
 
     A host-only build (the sanitizer build used in tests) lacks the device entry points;
     calling one of those raises AttributeError from ctypes, so nothing falls back silently.

@@ -299,6 +299,28 @@ def test_device_entry_points_reject_bad_arguments_without_launching():
     fg.fg_blocked_cache_destroy(h)
 
 
+def test_unaligned_pointers_rejected_without_launching():
+    """Every kernel moves 16 bytes per access: pools, new rows, q, out and the workspace must
+    be 16-byte aligned, and a pointer that is not is refused before anything is launched
+    (the pointers below are never dereferenced)."""
+    assert _status(fg.fg_blocked_cache_init, 8, 64, 1, 128, "bf16", 0x1008, 0x2000) == fg.FG_E_ARG
+    assert _status(fg.fg_blocked_cache_init, 8, 64, 1, 128, "bf16", 0x1000, 0x2002) == fg.FG_E_ARG
+    h = fg.fg_blocked_cache_init(8, 64, 1, 128, "bf16", 0x1000, 0x2000)
+    dev = fg.FgRaggedBatch()
+    dev.num_seqs, dev.num_tokens = 1, 4
+    dev.query_start = dev.n_query = dev.context_len = dev.block_table = \
+        fg.ctypes.cast(0x3000, fg.ctypes.POINTER(fg.ctypes.c_int32))
+    assert _status(fg.fg_kv_append, h, dev, 0x4008, 0x5000, None) == fg.FG_E_ARG
+    assert _status(fg.fg_kv_append, h, dev, 0x4000, 0x5004, None) == fg.FG_E_ARG
+    info = fg.FgPlanInfo()
+    for q, out, ws in ((0x4002, 0x5000, 0x6000), (0x4000, 0x5008, 0x6000),
+                       (0x4000, 0x5000, 0x6004)):
+        assert _status(fg.fg_ragged_attention, h, dev, info, 0x7000, q, 1, 1.0, out, ws, 64,
+                       None) == fg.FG_E_ARG
+    assert "aligned" in fg.fg_last_error()
+    fg.fg_blocked_cache_destroy(h)
+
+
 # --------------------------------------------------------------------------------------
 # attention work list
 # --------------------------------------------------------------------------------------
