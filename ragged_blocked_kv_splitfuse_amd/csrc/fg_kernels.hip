@@ -462,7 +462,7 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
 }
 
 // ---------------------------------------------------------------------------------------
-// MODE_TILE: up to 128 query rows (chunk rows).  Wave w owns rows [32w, 32w+32) as one
+// MODE_TILE: up to TILE_ROWS query rows (chunk rows).  Wave w owns rows [32w, 32w+32) as one
 // 32-row tile of the 32x32x16 MFMA.  Keys advance in 32-key stages; each stage's K [32 keys]
 // [128] and V^T [128][32 keys] are fetched straight from HBM into LDS (global_load_lds_dwordx4,
 // no register staging) through a ring of NSTAGE buffers, NSTAGE-1 stages ahead of the math, so
