@@ -996,15 +996,18 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// KV append: one workgroup per (tile of 64 consecutive new tokens, KV head).  K rows are
+// KV append: one workgroup per (tile of TOK consecutive new tokens, KV head).  K rows are
 // copied whole in 16-byte chunks (a K block row is contiguous).  V rows are staged in LDS
 // and written feature by feature with lanes on consecutive tokens, so the tokens of a prompt
 // chunk that share a block fill consecutive slots of each feature row (coalesced stores).
+// TOK is 64, 32 or 16: the largest that still gives APPEND_MIN_WGS workgroups, so that a
+// small pass (a few hundred decode tokens, or a 512-token chunk) still spreads over the chip.
 // ---------------------------------------------------------------------------------------
-constexpr int APPEND_TOKENS = 64;
+constexpr int APPEND_THREADS = 256;
+constexpr int64_t APPEND_MIN_WGS = 1024;  // four per compute unit
 
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void kv_append_kernel(
+template <typename T, int HD, int TOK>
+__global__ __launch_bounds__(APPEND_THREADS) void kv_append_kernel(
     const int32_t *__restrict__ query_start, const int32_t *__restrict__ context_len,
     const int32_t *__restrict__ block_table, int32_t table_stride, int32_t num_seqs,
     int32_t num_tokens, const T *__restrict__ k_new, const T *__restrict__ v_new,
@@ -1013,10 +1016,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   constexpr int VEC = 16 / sizeof(T);            // elements per 16-byte chunk
   constexpr int CPR = HD / VEC;                  // chunks per row
   constexpr int ROWP = HD + 4 / sizeof(T);       // LDS row padded by one dword
-  __shared__ int dblk[APPEND_TOKENS], dslot[APPEND_TOKENS];
-  __shared__ T vt[APPEND_TOKENS * ROWP];
-  const int t0 = blockIdx.x * APPEND_TOKENS, h = blockIdx.y, tid = threadIdx.x;
-  if (tid < APPEND_TOKENS) {
+  __shared__ int dblk[TOK], dslot[TOK];
+  __shared__ T vt[TOK * ROWP];
+  const int t0 = blockIdx.x * TOK, h = blockIdx.y, tid = threadIdx.x;
+  if (tid < TOK) {
     const int t = t0 + tid;
     int blk = -1, slot = 0;
     if (t < num_tokens) {
@@ -1037,7 +1040,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   }
   __syncthreads();
   const size_t row_in = (size_t)Hkv * HD;  // elements per token in k_new / v_new
-  for (int q = tid; q < APPEND_TOKENS * CPR; q += blockDim.x) {
+  for (int q = tid; q < TOK * CPR; q += APPEND_THREADS) {
     const int tok = q / CPR, c = q % CPR;
     const int blk = dblk[tok];
     if (blk < 0) continue;
@@ -1045,7 +1048,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     *reinterpret_cast<uint4 *>(k_pool + (((size_t)blk * Hkv + h) * bs + dslot[tok]) * HD +
                                c * VEC) = v;
   }
-  for (int q = tid; q < APPEND_TOKENS * CPR; q += blockDim.x) {
+  for (int q = tid; q < TOK * CPR; q += APPEND_THREADS) {
     const int tok = q / CPR, c = q % CPR;
     if (t0 + tok >= num_tokens) continue;
     const uint4 v = *reinterpret_cast<const uint4 *>(v_new + (t0 + tok) * row_in + h * HD + c * VEC);
@@ -1056,11 +1059,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     dst[3] = v.w;
   }
   __syncthreads();
-  const int tok = tid % APPEND_TOKENS;
+  const int tok = tid % TOK;
   const int blk = dblk[tok];
   if (blk < 0) return;
   T *vrow = v_pool + ((size_t)blk * Hkv + h) * HD * bs + dslot[tok];
-  for (int d = tid / APPEND_TOKENS; d < HD; d += blockDim.x / APPEND_TOKENS)
+  for (int d = tid / TOK; d < HD; d += APPEND_THREADS / TOK)
     vrow[(size_t)d * bs] = vt[tok * ROWP + d];
 }
 
@@ -1085,14 +1088,23 @@ fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const 
     return fail(FG_E_ARG, "k_new and v_new must be 16-byte aligned");
   const fg_cache_config &c = cache->cfg;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid((dev->num_tokens + APPEND_TOKENS - 1) / APPEND_TOKENS, c.num_kv_heads);
-  const dim3 block(256);
-#define FG_APPEND(T, HD)                                                                      \
-  hipLaunchKernelGGL((kv_append_kernel<T, HD>), grid, block, 0, st, dev->query_start,           \
+  int tok = 64;  // largest tile that still fills the chip (see kv_append_kernel)
+  while (tok > 16 && (int64_t)((dev->num_tokens + tok - 1) / tok) * c.num_kv_heads < APPEND_MIN_WGS)
+    tok /= 2;
+  const dim3 grid((dev->num_tokens + tok - 1) / tok, c.num_kv_heads);
+  const dim3 block(APPEND_THREADS);
+#define FG_APPEND_TOK(T, HD, TOKC)                                                             \
+  hipLaunchKernelGGL((kv_append_kernel<T, HD, TOKC>), grid, block, 0, st, dev->query_start,     \
                      dev->context_len, dev->block_table, dev->table_stride, dev->num_seqs,     \
                      dev->num_tokens, (const T *)k_new, (const T *)v_new, (T *)cache->k_pool,  \
                      (T *)cache->v_pool, c.num_kv_heads, c.block_size, cache->bs_log2,         \
                      c.num_blocks)
+#define FG_APPEND(T, HD)                                                                      \
+  do {                                                                                        \
+    if (tok == 64) FG_APPEND_TOK(T, HD, 64);                                                  \
+    else if (tok == 32) FG_APPEND_TOK(T, HD, 32);                                             \
+    else FG_APPEND_TOK(T, HD, 16);                                                            \
+  } while (0)
   if (c.dtype == FG_BF16)
     FG_APPEND(u16, 128);
   else if (c.head_dim == 64)
@@ -1100,6 +1112,7 @@ fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const 
   else
     FG_APPEND(float, 128);
 #undef FG_APPEND
+#undef FG_APPEND_TOK
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_E_HIP, "kv_append launch: %s", hipGetErrorString(e));
   return FG_OK;
