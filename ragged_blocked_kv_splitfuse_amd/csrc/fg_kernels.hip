@@ -377,21 +377,30 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
         for (int dc = 0; dc < D / 32; ++dc) kf[kh][a][dc] = as_bf16x8(ld16(kp + 32 * dc));
       }
     // ---- V^T operand: 8 consecutive keys of one feature per lane ------------------------
+    // A feature row of a V block is one 128-byte line at blocks of 64 keys; the two key
+    // halves (kh) read its two 64-byte halves.  They are requested by consecutive
+    // instructions, so that the second finds the line still in flight or cached: requested
+    // 8 instructions apart, a line is sometimes evicted in between and fetched again.
     uint4 vr[2][D / 16];
+    const u16 *vp[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const int key0 = k0 + 32 * kh + 8 * g;
-      int keyc = key0, blk = blk_t;
+      int keyc = k0 + 32 * kh + 8 * g, blk = blk_t;
       if (!BIG) {
         keyc = v_key(k0, kh);
         blk = blk_v[kh];
       }
-      const u16 *vp = P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (keyc & bs_mask) +
-                      (size_t)r * P.bs;
+      vp[kh] = P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (keyc & bs_mask) +
+               (size_t)r * P.bs;
+    }
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) vr[kh][dt] = ld16(vp + (size_t)16 * dt * P.bs);
-      if (k0 + KT > R.khi) {  // keys at or past khi: zero V so stale bits cannot reach O
-        const int nvalid = min(max(R.khi - key0, 0), 8);
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) vr[kh][dt] = ld16(vp[kh] + (size_t)16 * dt * P.bs);
+    if (k0 + KT > R.khi) {  // keys at or past khi: zero V so stale bits cannot reach O
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int nvalid = min(max(R.khi - (k0 + 32 * kh + 8 * g), 0), 8);
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) vr[kh][dt] = keep_first(vr[kh][dt], nvalid);
       }
