@@ -60,3 +60,40 @@ def test_random_pass(seed):
     assert np.array_equal(G.to_host_bits(r["gp"].cache.k_pool, "bf16").view(dt), r["k_pool"].view(dt))
     assert np.array_equal(G.to_host_bits(r["gp"].cache.v_pool, "bf16").view(dt), r["v_pool"].view(dt))
     G.assert_close(G.out_to_f64(r["out"]), r["ref"], "bf16", f"random[{seed}]")
+
+
+def draw_case_f32(seed):
+    """A seeded random fp32 pass shape (the accuracy path): head dims 64 and 128, small blocks."""
+    rng = np.random.Generator(np.random.PCG64(95000 + seed))
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([2, 8, 16, 64]))
+    n_decode = int(rng.integers(0, 5))
+    lo = int(rng.integers(0, 100))
+    hi = lo + int(rng.integers(0, 600))
+    prompts = []
+    for _ in range(int(rng.integers(1, 3))):
+        L = int(rng.integers(1, 400))
+        c = int(rng.integers(0, L)) if rng.random() < 0.5 else 0
+        prompts.append((c, L))
+    demand = n_decode + sum(L - c for c, L in prompts)
+    budget = int(rng.integers(max(1, n_decode), min(demand, 160) + 1))
+    # fp32 rounding of the logits is amplified by the exponential: with a logit spread of 8
+    # plain fp32 arithmetic already lands ~1e-5 from the float64 result at head_dim 128, so
+    # the steeper draws here stop at a spread of 3.
+    q_scale = float(rng.choice([1.0, 3.0]))
+    return dict(dtype="f32", hq=hkv * g, hkv=hkv, d=d, bs=bs, budget=budget, n_decode=n_decode,
+                decode_ctx=(lo, hi), prompts=tuple(prompts), q_scale=q_scale)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_pass_f32(seed):
+    kw = draw_case_f32(seed)
+    G.say(f"random fp32 case {seed}: {kw}")
+    w = wl.custom(80000 + seed, **kw)
+    r = G.full_pass(w)
+    dt = np.uint32
+    assert np.array_equal(G.to_host_bits(r["gp"].cache.k_pool, "f32").view(dt), r["k_pool"].view(dt))
+    assert np.array_equal(G.to_host_bits(r["gp"].cache.v_pool, "f32").view(dt), r["v_pool"].view(dt))
+    G.assert_close(G.out_to_f64(r["out"]), r["ref"], "f32", f"random_f32[{seed}]")
