@@ -193,6 +193,14 @@ class DevicePass:
         self.out = None
         self.timing, self.marks = bool(timing), []
         self.proj = proj
+        self.events, self.ev_next = [], 0  # timing events created ahead (reserve_events)
+
+    def reserve_events(self, n_passes: int):
+        """Create the timing events of n_passes passes now, so that creating them does not
+        count in the host time of the passes that record them."""
+        import torch
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(5 * int(n_passes))]
+        self.ev_next = 0
 
     def __call__(self, hb, running):
         import torch
@@ -207,7 +215,11 @@ class DevicePass:
         ev = None
         if self.timing:
             st = self.stream or torch.cuda.current_stream()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            if self.ev_next + 5 <= len(self.events):
+                ev = self.events[self.ev_next:self.ev_next + 5]
+                self.ev_next += 5
+            else:
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
             ev[0].record(st)
         if self.proj is not None:
             x = self.rows(hb, running)
