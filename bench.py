@@ -65,6 +65,11 @@ def parse():
                     help="chunked workload: which 512-token pass (0..31) a step runs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--per-config", type=int, default=1,
+                    help="also time the decode-only, chunked (pass --chunk-pass) and Mistral "
+                         "passes and report them in a per_config block (0 = headline only)")
+    ap.add_argument("--per-config-steps", type=int, default=20,
+                    help="timed steps of each per_config pass")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--num-cus", type=int, default=0,
                     help="compute units the attention planner sizes splits for (0 = device's)")
@@ -80,13 +85,13 @@ def parse():
     return ap.parse_args()
 
 
-def setup(args):
+def setup(args, workload=None):
     import numpy as np
     import torch
     from ragged_blocked_kv_splitfuse_amd import fg, workloads as wl
     from ragged_blocked_kv_splitfuse_amd.runtime import PagedKVCache, num_cus
 
-    cfg = WORKLOADS[args.workload]
+    cfg = WORKLOADS[workload or args.workload]
     w = wl.make(cfg, args.seed)
     init_states = w.fresh_states()
     free_ids = np.asarray(w.free_ids, np.int32)
@@ -289,28 +294,19 @@ def main():
     q, k_new, v_new, host_s = r["q"], r["k_new"], r["v_new"], r["host_s"]
     value = T * args.steps / elapsed
 
-    if w.dtype == "bf16" and args.workload != "chunked":
-        roof = {"bound": "hbm", "achieved": attn_bytes / t_attn / 1e9, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
-    elif w.dtype == "bf16":
-        roof = {"bound": "mfma", "achieved": attn_flops / t_attn / 1e12, "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "alu", "achieved": attn_flops / t_attn / 1e12,
-                "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        rec = tr.get(args.workload)
-        if rec and rec.get("kernel_source") == kernel_source_hash():
-            roof["traffic"] = rec["bytes_per_launch"]
-    roof["kernel"] = "attention_bf16_kernel" if w.dtype == "bf16" else "attention_f32_kernel"
-    roof["algorithmic_bytes"] = attn_bytes
-    roof["algorithmic_flops"] = attn_flops
-    roof["mfma_frac"] = attn_flops / t_attn / 1e12 / BF16_PEAK_TFLOPS
-
+    roof = roofline(w, args.workload, attn_bytes, attn_flops, t_attn)
+    per_config = None
+    if args.per_config and args.workload == "llama2":
+        per_config = {"llama2": config_entry(w, r, "hbm")}
+        del S, r
+        torch.cuda.empty_cache()
+        for name, bound in (("decode", "hbm"), ("chunked", "mfma"), ("mistral", "hbm+mfma")):
+            P = setup(args, name)
+            rr = time_pass(P, args.per_config_steps, min(args.warmup, 3))
+            per_config[name] = config_entry(P["w"], rr, bound)
+            print(json.dumps({"per_config": name, **per_config[name]}), file=sys.stderr, flush=True)
+            del P, rr
+            torch.cuda.empty_cache()
     result = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3,
@@ -322,6 +318,8 @@ def main():
                    "decode_seqs": int((nq == 1).sum()), "work_records": int(info.num_work),
                    "split_groups": int(info.num_groups)},
         "roofline": roof,
+        "per_config": per_config,
+        "hbm_reference": hbm_reference() if args.per_config else None,
         "kernels": {"attention_us": t_attn * 1e6, "kv_append_us": t_app * 1e6,
                     "kv_append_GBps": append_bytes / t_app / 1e9,
                     "gpu_only_tokens_per_s": T / (t_attn + t_app),
@@ -338,7 +336,8 @@ def serving_main(args):
     import torch
     from ragged_blocked_kv_splitfuse_amd import fg, workloads as wl
     from ragged_blocked_kv_splitfuse_amd.runtime import PagedKVCache, num_cus
-    from ragged_blocked_kv_splitfuse_amd.serving import DevicePass, ServingLoop
+    from ragged_blocked_kv_splitfuse_amd.serving import (DevicePass, ServingLoop,
+                                                         latency_summary, request_latencies)
 
     hkv = 32 if args.model == "llama2" else 8
     sw = wl.serving_stream(seed=args.seed if args.seed is not None else 6,
@@ -399,27 +398,9 @@ def serving_main(args):
     total = int(T.sum())
     gpu_pass = seg.sum(axis=1)
 
-    def latencies(end_times):
-        """Per request: time to first token (from joining -- the end of the pass before its
-        admission pass -- to the end of its first-token pass) and the mean gap between its
-        generated tokens."""
-        start = lambda p: 0.0 if p == 0 else float(end_times[p - 1])
-        ttft, pace = [], []
-        for r in sw.requests:
-            a, f, e = st.admit_pass[r.rid], st.first_token_pass[r.rid], st.finish_pass[r.rid]
-            ttft.append(float(end_times[f]) - start(a))
-            pace.append((float(end_times[e]) - float(end_times[f])) / (r.output_len - 1)
-                        if r.output_len > 1 else np.nan)
-        return np.array(ttft), np.array(pace)
-
     def summary(end_times):
-        ttft, pace = latencies(end_times)
-        pc = pace[~np.isnan(pace)]
-        return {"ttft_ms_mean": float(ttft.mean() * 1e3),
-                "ttft_ms_p50": float(np.percentile(ttft, 50) * 1e3),
-                "ttft_ms_p95": float(np.percentile(ttft, 95) * 1e3),
-                "token_pace_ms_mean": float(pc.mean() * 1e3),
-                "token_pace_ms_p95": float(np.percentile(pc, 95) * 1e3)}
+        ttft, pace = request_latencies(st, sw.requests, end_times)
+        return latency_summary(ttft, pace)
 
     ttft_p = [st.first_token_pass[r.rid] - st.admit_pass[r.rid] + 1 for r in sw.requests]
     serving = {"passes": st.passes, "tokens": total,
@@ -443,12 +424,6 @@ def serving_main(args):
     proxy = {"layers": L, "includes": "kv_append + attention" + (" + QKV/O projections"
                                                                  if proj is not None else ""),
              "tokens_per_s": total / float(proxy_ends[-1]), **summary(proxy_ends)}
-    # share of requests meeting both a first-token and a token-pace threshold (the pages give
-    # no thresholds: a grid of them)
-    ttft_px, pace_px = latencies(proxy_ends)
-    ok_pace = lambda b: np.isnan(pace_px) | (pace_px <= b)
-    proxy["sla_attainment"] = {f"ttft<={a}s,pace<={b}s": float(np.mean((ttft_px <= a) & ok_pace(b)))
-                               for a in (0.5, 1.0, 2.0) for b in (0.025, 0.05, 0.1)}
     result = {
         "metric": "serving-loop tokens/s (continuous SplitFuse passes, whole request stream)",
         "value": total / wall, "unit": "tokens/s", "n_gpus": 1, "steps": st.passes,
@@ -466,6 +441,107 @@ def serving_main(args):
         "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)
+
+
+def roofline(w, workload, attn_bytes, attn_flops, t_attn):
+    """Roofline of the dominant kernel (attention): HBM for the decode-heavy and mixed passes,
+    bf16 MFMA for the chunked pass, fp32 VALU for fp32 inputs."""
+    if w.dtype == "bf16" and workload != "chunked":
+        roof = {"bound": "hbm", "achieved": attn_bytes / t_attn / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    elif w.dtype == "bf16":
+        roof = {"bound": "mfma", "achieved": attn_flops / t_attn / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "alu", "achieved": attn_flops / t_attn / 1e12,
+                "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        rec = tr.get(workload)
+        if rec and rec.get("kernel_source") == kernel_source_hash():
+            roof["traffic"] = rec["bytes_per_launch"]
+    roof["kernel"] = "attention_bf16_kernel" if w.dtype == "bf16" else "attention_f32_kernel"
+    roof["algorithmic_bytes"] = attn_bytes
+    roof["algorithmic_flops"] = attn_flops
+    roof["mfma_frac"] = attn_flops / t_attn / 1e12 / BF16_PEAK_TFLOPS
+    return roof
+
+
+def config_entry(w, r, bound):
+    """One pass shape's figures: kernel times (HIP events on the launch stream), algorithmic
+    bytes and flops of attention, and the fraction of the bounding roofline.  For a mixed
+    pass ("hbm+mfma") the roofline time is max(bytes / HBM peak, flops / MFMA peak)."""
+    t_attn, t_app = r["t_attn"], r["t_app"]
+    B, F = r["attn_bytes"], r["attn_flops"]
+    hbm = B / t_attn / 1e9 / HBM_PEAK_GBS
+    mfma = F / t_attn / 1e12 / BF16_PEAK_TFLOPS
+    t_roof = max(B / (HBM_PEAK_GBS * 1e9), F / (BF16_PEAK_TFLOPS * 1e12))
+    frac = {"hbm": hbm, "mfma": mfma, "hbm+mfma": t_roof / t_attn}[bound]
+    return {"workload": w.name, "tokens": r["T"], "num_seqs": r["nseq"],
+            "ms": (t_attn + t_app) * 1e3, "attention_us": t_attn * 1e6,
+            "kv_append_us": t_app * 1e6, "algorithmic_bytes": B, "algorithmic_flops": F,
+            "append_bytes": r["append_bytes"], "bound": bound, "frac": frac, "hbm_frac": hbm,
+            "mfma_frac": mfma, "kv_append_hbm_frac": r["append_bytes"] / t_app / 1e9 / HBM_PEAK_GBS,
+            "gpu_only_tokens_per_s": r["T"] / (t_attn + t_app),
+            "step_tokens_per_s": r["T"] * len(r["host_s"]) / r["elapsed"],
+            "split_groups": int(r["info"].num_groups), "work_records": int(r["info"].num_work)}
+
+
+def hbm_reference(gib=4, reps=10):
+    """Practical HBM rates on this device, measured beside the pass: a device-to-device copy
+    of `gib` GiB (bytes read + written per second) and a read-only reduction of 2*`gib` GiB
+    (torch's own kernels), both timed with events over `reps` repetitions."""
+    import torch
+    n = gib << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    x = torch.empty(2 * n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    out = {}
+    for name, fn, nbytes in (("copy", lambda: b.copy_(a), 2 * n),
+                             ("read", lambda: x.sum(), 2 * n)):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_GBps"] = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b, x
+    torch.cuda.empty_cache()
+    out["how"] = (f"torch device copy of {gib} GiB (read + write bytes) and torch sum over "
+                  f"{2 * gib} GiB of fp32 (read bytes), {reps} repetitions each")
+    return out
+
+
+def host_identity():
+    """CPU model, logical CPUs this process may use, and numpy's BLAS build."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = libs[0]
+            blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '')}, " \
+                   f"{i.get('architecture', '')}, {i.get('num_threads')} threads)"
+    except Exception:  # noqa: BLE001
+        pass
+    import numpy as np
+    return {"cpu_model": model, "cpus_allowed": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__, "blas": blas}
 
 
 def cpu_baseline(args, w, cache, hb, q, k_new, v_new):
@@ -509,7 +585,7 @@ def cpu_baseline(args, w, cache, hb, q, k_new, v_new):
     t = float(np.mean(times))
     full = t * w.num_kv_heads / hk
     return {"value": hb.num_tokens / full, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", **host_identity(),
             "sample": f"numpy fp64 oracle (append + attention) on {hk} of {w.num_kv_heads} KV "
                       f"heads of the same pass (all {S} sequences, {hb.num_tokens} tokens), "
                       f"{len(times)} run(s) of {t:.2f} s, scaled x{w.num_kv_heads / hk:g} to "

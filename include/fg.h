@@ -19,7 +19,11 @@
  *     new K/V, outputs, device copies of descriptors, the work list and the workspace.  The
  *     library owns only the opaque fg_cache handle and its free list (host memory).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
- *     enqueued asynchronously on it; no call allocates device memory or synchronises.
+ *     enqueued asynchronously on it.  No entry point of the pass (fg_kv_append,
+ *     fg_ragged_attention and their helpers) allocates device memory or synchronises, except
+ *     in validation mode (FG_VALIDATE=1, see fg_kv_append); the
+ *     one exception in this header is fg_linear_bf16, which creates its GEMM library handle
+ *     and a scratch buffer on first use (see there).
  *   - Every function returns fg_status and never aborts or throws across the ABI.  On an
  *     error nothing is launched and no state is changed, unless stated otherwise;
  *     fg_last_error() returns a thread-local message for the last failing call.
@@ -178,13 +182,31 @@ fg_status fg_splitfuse_retire(fg_cache *cache, fg_seq_state *seqs, int32_t n_seq
  * first violation in fg_last_error(). */
 fg_status fg_validate_batch(const fg_cache *cache, const fg_ragged_batch *host);
 
+/* Full check of a work list against the host batch and plan it was made for (host only):
+ * sizes consistent with the plan; every item's sequence, query tokens and key range inside
+ * that sequence (an unsplit item covers keys [0, c + last token + 1); the splits of a group
+ * are consecutive items whose key ranges tile that span in split order); every query token
+ * of every sequence in exactly one item; each item's split partials inside workspace_bytes;
+ * every (item, KV head) in exactly one attention record; every merge record naming split 0
+ * of one split group.  fg_ragged_attention runs this check on device copies when FG_VALIDATE
+ * is set (below).  FG_E_DESC names the first violation in fg_last_error(); FG_E_ARG for null
+ * arguments.  FG_F32 caches need no work list: FG_OK. */
+fg_status fg_validate_work(const fg_cache *cache, const fg_ragged_batch *host,
+                           const fg_attention_plan_info *plan, const int32_t *work,
+                           size_t workspace_bytes);
+
 /* ---- device work -------------------------------------------------------------------- */
 
 /* Appends the pass's new rows: new token i of sequence s (position context_len[s]+i) goes
  * to block block_table[s][pos / block_size], slot pos % block_size, of both pools.  A bit
  * copy; no other element of either pool is written.  `dev` arrays are device memory.
  * k_new, v_new: device [T][Hkv][D], 16-byte aligned.  Errors: FG_E_ARG (null or unaligned
- * pointers, negative sizes), FG_E_HIP. */
+ * pointers, negative sizes), FG_E_DESC (FG_VALIDATE only), FG_E_HIP.
+ * Validation mode: with the environment variable FG_VALIDATE=1 (read at every call) the
+ * descriptors are first copied back to the host on `stream` -- which synchronises the stream
+ * -- and checked as fg_validate_batch does; on a violation nothing is launched and FG_E_DESC
+ * is returned.  Without it only cheap argument checks run and block ids are clamped into the
+ * pool, so a bad table cannot make the kernel write outside the pools. */
 fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const void *k_new,
                        const void *v_new, void *stream);
 
@@ -206,6 +228,14 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *host,
                             fg_attention_plan_info *info, int32_t *work,
                             int32_t work_capacity);
 
+/* Device workspace (bytes) fg_ragged_attention needs for this host batch when planned with
+ * fg_attention_plan for num_q_heads and num_cus: the same figure as plan->workspace_bytes,
+ * without writing a work list.  0 when the plan splits no key range.  Errors as
+ * fg_attention_plan (FG_E_ARG also for a null `bytes`). */
+fg_status fg_ragged_attention_workspace_size(const fg_cache *cache, const fg_ragged_batch *host,
+                                             int32_t num_q_heads, int32_t num_cus,
+                                             size_t *bytes);
+
 /* Exact causal attention of every new token over its sequence's cached history (keys
  * 0 .. context_len[s] + i for new token i, which includes the rows fg_kv_append just
  * wrote): out[t][g] = sum_j softmax_j(scale * q[t][g] . K_j) V_j.  bf16 inputs: products
@@ -218,7 +248,10 @@ fg_status fg_attention_plan(const fg_cache *cache, const fg_ragged_batch *host,
  * (its contents are scratch); calls sharing a workspace must be ordered on one stream.
  * Results are deterministic (no atomics; merges run in split order).  q, out and workspace
  * must be 16-byte aligned.
- * Errors: FG_E_ARG, FG_E_UNSUPPORTED, FG_E_WORKSPACE, FG_E_HIP. */
+ * Validation mode (FG_VALIDATE=1, as for fg_kv_append): the descriptors and the work list are
+ * copied back on `stream` (synchronising it) and checked with fg_validate_batch and
+ * fg_validate_work before anything is launched; a violation returns FG_E_DESC.
+ * Errors: FG_E_ARG, FG_E_DESC (FG_VALIDATE only), FG_E_UNSUPPORTED, FG_E_WORKSPACE, FG_E_HIP. */
 fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
                               const fg_attention_plan_info *plan, const int32_t *work_dev,
                               const void *q, int32_t num_q_heads, float scale, void *out,
@@ -233,9 +266,10 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
  * attention rows.  y[T][N] = x[T][K] . w[N][K]^T (w in the [out][in] layout of a linear
  * layer), all three bf16, device memory, row-major and dense; fp32 accumulation, one rounding
  * to bf16 (nearest even) per output.  A plain GEMM, run by hipBLASLt.  The first call on a
- * device creates its hipBLASLt handle and a 32 MiB workspace (kept until the process ends);
- * the first call for a (T, K, N) also picks the algorithm.  Calls on one device serialise on a
- * lock.  Errors: FG_E_ARG (null pointer, T < 0, K or N < 1), FG_E_UNSUPPORTED (no algorithm),
+ * device creates its hipBLASLt handle, and the first call on each (device, stream) a 32 MiB
+ * workspace for that stream (all kept until the process ends), so calls on different streams
+ * never share scratch memory; the first call for a (T, K, N) also picks the algorithm.  Host
+ * calls serialise on a lock.  Errors: FG_E_ARG (null pointer, T < 0, K or N < 1), FG_E_UNSUPPORTED (no algorithm),
  * FG_E_HIP (a hipBLASLt or HIP error).  T = 0 does nothing. */
 fg_status fg_linear_bf16(const void *x, const void *w, void *y, int32_t T, int32_t K, int32_t N,
                          void *stream);

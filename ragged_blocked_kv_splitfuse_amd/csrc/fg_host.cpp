@@ -316,6 +316,139 @@ fg_status fg_validate_batch(const fg_cache *cache, const fg_ragged_batch *b) {
 }
 
 // --------------------------------------------------------------------------------------
+// work-list validation and workspace sizing
+// --------------------------------------------------------------------------------------
+
+fg_status fg_validate_work(const fg_cache *cache, const fg_ragged_batch *b,
+                           const fg_attention_plan_info *plan, const int32_t *work,
+                           size_t workspace_bytes) {
+  clear_error();
+  if (!cache || !b || !plan) return fail(FG_E_ARG, "null argument");
+  if (cache->cfg.dtype == FG_F32) return FG_OK;  // the fp32 kernel reads no work list
+  const int32_t Hkv = cache->cfg.num_kv_heads, D = cache->cfg.head_dim;
+  const int32_t Hq = plan->num_q_heads;
+  if (Hq < 1 || Hq % Hkv) return fail(FG_E_DESC, "plan num_q_heads %d", Hq);
+  const int32_t G = Hq / Hkv, S = b->num_seqs;
+  if (plan->num_tokens != b->num_tokens)
+    return fail(FG_E_DESC, "plan made for %d tokens, batch has %d", plan->num_tokens,
+                b->num_tokens);
+  if (S < 0 || (S > 0 && (!b->n_query || !b->context_len)))
+    return fail(FG_E_DESC, "batch arrays are null");
+  const int64_t NI = plan->num_items, NW = plan->num_work, NG = plan->num_groups;
+  if (NI < 0 || NW < 0 || NG < 0 || NG > NW ||
+      (int64_t)plan->work_ints != NI * FG_ITEM_INTS + NW)
+    return fail(FG_E_DESC, "inconsistent plan sizes (items %lld, records %lld, groups %lld)",
+                (long long)NI, (long long)NW, (long long)NG);
+  if (plan->workspace_bytes > 0 && workspace_bytes < (size_t)plan->workspace_bytes)
+    return fail(FG_E_DESC, "workspace of %zu bytes, plan needs %lld", workspace_bytes,
+                (long long)plan->workspace_bytes);
+  if (plan->work_ints > 0 && !work) return fail(FG_E_ARG, "work is null");
+  const int64_t ws_floats = (int64_t)(workspace_bytes / 4);
+  // items: ranges inside their sequence, partial slots inside the workspace
+  std::vector<int64_t> seq_rows(S, 0);  // query tokens x key coverage, checked below
+  for (int64_t i = 0; i < NI; ++i) {
+    const int32_t *w = work + i * FG_ITEM_INTS;
+    const int32_t s = w[I_SEQ], t0 = w[I_TOK0], nt = w[I_NTOK], klo = w[I_KLO], khi = w[I_KHI];
+    const int32_t mode = w[I_MODE], grp = w[I_GROUP], sp = w[I_SPLIT], ns = w[I_NSPLIT];
+    if (s < 0 || s >= S) return fail(FG_E_DESC, "item %lld: sequence %d of %d", (long long)i, s, S);
+    const int64_t c = b->context_len[s], n = b->n_query[s];
+    if (t0 < 0 || nt < 1 || t0 + (int64_t)nt > n)
+      return fail(FG_E_DESC, "item %lld: tokens [%d, %d) outside [0, %lld)", (long long)i, t0,
+                  t0 + nt, (long long)n);
+    if (mode != MODE_STREAM && mode != MODE_TILE)
+      return fail(FG_E_DESC, "item %lld: mode %d", (long long)i, mode);
+    const int64_t cap = mode == MODE_STREAM ? STREAM_ROWS : TILE_ROWS;
+    if ((int64_t)nt * G > cap)
+      return fail(FG_E_DESC, "item %lld: %lld rows > %lld", (long long)i, (long long)nt * G,
+                  (long long)cap);
+    if (klo < 0 || klo % KEY_TILE || khi <= klo || khi > c + t0 + nt)
+      return fail(FG_E_DESC, "item %lld: key range [%d, %d) (last row sees %lld keys)",
+                  (long long)i, klo, khi, (long long)(c + t0 + nt));
+    if (grp < 0) {
+      if (klo != 0 || khi != c + t0 + nt || sp != 0 || ns != 1)
+        return fail(FG_E_DESC, "item %lld: unsplit item must cover keys [0, %lld)", (long long)i,
+                    (long long)(c + t0 + nt));
+      seq_rows[s] += nt;
+    } else {
+      if (ns < 2 || sp < 0 || sp >= ns || (int64_t)grp + Hkv > NG)
+        return fail(FG_E_DESC, "item %lld: split %d of %d, group %d of %lld", (long long)i, sp,
+                    ns, grp, (long long)NG);
+      const int64_t slot = slot_floats(mode, D);
+      const int64_t poff = w[I_POFF];
+      if (poff < 0 || poff + (int64_t)Hkv * ns * slot > ws_floats)
+        return fail(FG_E_DESC, "item %lld: partials [%lld, %lld) floats outside the workspace",
+                    (long long)i, (long long)poff, (long long)(poff + (int64_t)Hkv * ns * slot));
+      if (sp == 0) seq_rows[s] += nt;
+    }
+  }
+  // splits of a group: consecutive items, contiguous key ranges covering [0, last row's keys)
+  for (int64_t i = 0; i < NI; ++i) {
+    const int32_t *w = work + i * FG_ITEM_INTS;
+    if (w[I_GROUP] < 0 || w[I_SPLIT] != 0) continue;
+    const int32_t ns = w[I_NSPLIT];
+    if (i + ns > NI) return fail(FG_E_DESC, "item %lld: group runs past the list", (long long)i);
+    int32_t next = 0;
+    for (int32_t k = 0; k < ns; ++k) {
+      const int32_t *u = work + (i + k) * FG_ITEM_INTS;
+      if (u[I_GROUP] != w[I_GROUP] || u[I_SPLIT] != k || u[I_NSPLIT] != ns ||
+          u[I_SEQ] != w[I_SEQ] || u[I_TOK0] != w[I_TOK0] || u[I_NTOK] != w[I_NTOK] ||
+          u[I_MODE] != w[I_MODE] || u[I_POFF] != w[I_POFF] || u[I_KLO] != next)
+        return fail(FG_E_DESC, "item %lld: split %d of its group is inconsistent",
+                    (long long)(i + k), k);
+      next = u[I_KHI];
+    }
+    const int64_t want = (int64_t)b->context_len[w[I_SEQ]] + w[I_TOK0] + w[I_NTOK];
+    if (next != want)
+      return fail(FG_E_DESC, "item %lld: splits end at key %d, rows need %lld", (long long)i,
+                  next, (long long)want);
+  }
+  for (int32_t s = 0; s < S; ++s)
+    if (seq_rows[s] != b->n_query[s])
+      return fail(FG_E_DESC, "sequence %d: items cover %lld of %d query tokens", s,
+                  (long long)seq_rows[s], b->n_query[s]);
+  // records: every (item, KV head) exactly once among the attention records; merge records
+  // name split 0 of each group's head
+  const int32_t *codes = work + NI * FG_ITEM_INTS;
+  std::vector<uint8_t> seen((size_t)(NI * Hkv), 0);
+  for (int64_t r = 0; r < NW - NG; ++r) {
+    const int32_t code = codes[r];
+    if (code == -1) continue;
+    if (code < 0 || code >= NI * Hkv)
+      return fail(FG_E_DESC, "record %lld: code %d out of range", (long long)r, code);
+    if (seen[code]++) return fail(FG_E_DESC, "record %lld: code %d repeated", (long long)r, code);
+  }
+  for (int64_t k = 0; k < NI * Hkv; ++k)
+    if (!seen[k]) return fail(FG_E_DESC, "item %lld, KV head %lld has no record",
+                              (long long)(k / Hkv), (long long)(k % Hkv));
+  std::vector<uint8_t> gseen((size_t)NG, 0);
+  for (int64_t r = NW - NG; r < NW; ++r) {
+    const int32_t code = codes[r];
+    if (code < 0 || code >= NI * Hkv)
+      return fail(FG_E_DESC, "merge record %lld: code %d out of range", (long long)r, code);
+    const int32_t *w = work + (int64_t)(code / Hkv) * FG_ITEM_INTS;
+    const int64_t g = w[I_GROUP] >= 0 ? (int64_t)w[I_GROUP] + code % Hkv : -1;
+    if (g < 0 || w[I_SPLIT] != 0 || g >= NG || gseen[g]++)
+      return fail(FG_E_DESC, "merge record %lld: code %d names no split group once",
+                  (long long)r, code);
+  }
+  return FG_OK;
+}
+
+fg_status fg_ragged_attention_workspace_size(const fg_cache *cache, const fg_ragged_batch *host,
+                                             int32_t num_q_heads, int32_t num_cus,
+                                             size_t *bytes) {
+  if (!bytes) {
+    clear_error();
+    return fail(FG_E_ARG, "bytes is null");
+  }
+  *bytes = 0;
+  fg_attention_plan_info info;
+  const fg_status st = fg_attention_plan(cache, host, num_q_heads, num_cus, &info, nullptr, 0);
+  if (st == FG_OK) *bytes = (size_t)info.workspace_bytes;
+  return st;
+}
+
+// --------------------------------------------------------------------------------------
 // attention work list
 // --------------------------------------------------------------------------------------
 

@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
+#include <vector>
 
 #include "fg_internal.h"
 
@@ -519,15 +521,16 @@ struct Lds {
 };
 
 // One wave instruction: 16 bytes per lane from global memory to LDS at lds_wave_base + 16*lane.
-// Written as inline asm (M0 holds the wave's LDS base) so that the compiler does not track
-// these loads: its alias tracking of LDS-DMA targets is easily lost and then drains every
-// prefetched stage before ordinary LDS reads.  The kernel waits for the loads itself
-// (wait_dma) and separates them from LDS reads by barriers; the "memory" clobber keeps the
-// compiler from moving memory operations across them.  Nothing else in these kernels uses M0.
+// Written as inline asm so that the compiler does not track these loads: its alias tracking of
+// LDS-DMA targets is easily lost and then drains every prefetched stage before ordinary LDS
+// reads.  The LDS base goes in through an "{m0}" operand, so the compiler itself writes M0 and
+// knows it is in use.  The kernel waits for the loads itself (wait_dma) and separates them from
+// LDS reads by barriers; the "memory" clobber keeps the compiler from moving memory operations
+// across them.
 __device__ __forceinline__ void dma16(const u16 *src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("global_load_lds_dwordx4 %0, off"
                :
-               : "v"(src), "s"(lds_addr)
+               : "v"(src), "{m0}"(lds_addr)
                : "memory");
 }
 
@@ -1079,6 +1082,60 @@ __global__ __launch_bounds__(APPEND_THREADS) void kv_append_kernel(
 }  // namespace
 
 // =======================================================================================
+// Validation mode (FG_VALIDATE=1): copy the device descriptors (and work list) back on the
+// caller's stream and check them on the host before launching anything.
+// =======================================================================================
+namespace {
+
+bool validate_mode() {
+  const char *v = getenv("FG_VALIDATE");
+  return v && v[0] == '1' && v[1] == 0;
+}
+
+template <typename T>
+fg_status copy_back(std::vector<T> &dst, const T *src, size_t n, hipStream_t st) {
+  dst.resize(n ? n : 1);
+  if (!n) return FG_OK;
+  if (!src) return fail(FG_E_ARG, "descriptor array is null");
+  const hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return fail(FG_E_HIP, "validation copy: %s", hipGetErrorString(e));
+  return FG_OK;
+}
+
+// Host copy of a device batch (n_query derived from query_start when the device batch has
+// none), checked with fg_validate_batch; the copies stay in `h` for further checks.
+struct HostCopy {
+  std::vector<int32_t> qs, nq, cl, bt;
+  fg_ragged_batch b{};
+};
+
+fg_status validate_device_batch(const fg_cache *cache, const fg_ragged_batch *dev, hipStream_t st,
+                                HostCopy &h) {
+  const size_t S = (size_t)dev->num_seqs, W = (size_t)(dev->table_stride > 0 ? dev->table_stride : 0);
+  fg_status r;
+  if ((r = copy_back(h.qs, dev->query_start, S + 1, st)) != FG_OK) return r;
+  if (dev->n_query && (r = copy_back(h.nq, dev->n_query, S, st)) != FG_OK) return r;
+  if ((r = copy_back(h.cl, dev->context_len, S, st)) != FG_OK) return r;
+  if ((r = copy_back(h.bt, dev->block_table, S * W, st)) != FG_OK) return r;
+  const hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(FG_E_HIP, "validation sync: %s", hipGetErrorString(e));
+  if (!dev->n_query) {
+    h.nq.resize(S ? S : 1);
+    for (size_t s = 0; s < S; ++s) h.nq[s] = h.qs[s + 1] - h.qs[s];
+  }
+  h.b = *dev;
+  h.b.query_start = h.qs.data();
+  h.b.n_query = h.nq.data();
+  h.b.context_len = h.cl.data();
+  h.b.block_table = h.bt.data();
+  h.b.seq_index = nullptr;
+  h.b.seq_id = nullptr;
+  return fg_validate_batch(cache, &h.b);
+}
+
+}  // namespace
+
+// =======================================================================================
 // C ABI
 // =======================================================================================
 extern "C" {
@@ -1097,6 +1154,11 @@ fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const 
     return fail(FG_E_ARG, "k_new and v_new must be 16-byte aligned");
   const fg_cache_config &c = cache->cfg;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    HostCopy h;
+    const fg_status r = validate_device_batch(cache, dev, st, h);
+    if (r != FG_OK) return r;
+  }
   int tok = 64;  // largest tile that still fills the chip (see kv_append_kernel)
   while (tok > 16 && (int64_t)((dev->num_tokens + tok - 1) / tok) * c.num_kv_heads < APPEND_MIN_WGS)
     tok /= 2;
@@ -1148,6 +1210,21 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
        reinterpret_cast<uintptr_t>(workspace)) & 15)
     return fail(FG_E_ARG, "q, out and workspace must be 16-byte aligned");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (validate_mode()) {
+    HostCopy h;
+    fg_status r = validate_device_batch(cache, dev, st, h);
+    if (r != FG_OK) return r;
+    if (c.dtype == FG_BF16) {
+      if (!plan) return fail(FG_E_ARG, "bf16 attention needs the plan info");
+      std::vector<int32_t> work;
+      if ((r = copy_back(work, work_dev, (size_t)(plan->work_ints > 0 ? plan->work_ints : 0), st)) != FG_OK)
+        return r;
+      const hipError_t e = hipStreamSynchronize(st);
+      if (e != hipSuccess) return fail(FG_E_HIP, "validation sync: %s", hipGetErrorString(e));
+      h.b.num_tokens = dev->num_tokens;
+      if ((r = fg_validate_work(cache, &h.b, plan, work.data(), workspace_bytes)) != FG_OK) return r;
+    }
+  }
   if (c.dtype == FG_F32) {
     const dim3 grid((unsigned)dev->num_tokens * num_q_heads), block(64);
     if (c.head_dim == 64)

@@ -28,9 +28,11 @@ struct Plan {
   size_t ws = 0;
 };
 
+// One hipBLASLt handle and plan cache per device; one workspace per (device, stream), so that
+// GEMMs enqueued on different streams never share scratch memory while they may overlap.
 struct DeviceState {
   hipblasLtHandle_t handle = nullptr;
-  void *workspace = nullptr;
+  std::map<void *, void *> workspace;  // stream -> workspace
   std::map<std::tuple<int32_t, int32_t, int32_t>, Plan> plans;
 };
 
@@ -112,14 +114,12 @@ extern "C" fg_status fg_linear_bf16(const void *x, const void *w, void *y, int32
   if (hipGetDevice(&dev) != hipSuccess) return fail(FG_E_HIP, "hipGetDevice failed");
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceState &ds = g_dev[dev];
-  if (!ds.handle) {
-    BLAS_TRY(hipblasLtCreate(&ds.handle));
-    if (hipMalloc(&ds.workspace, WORKSPACE_BYTES) != hipSuccess) {
-      hipblasLtDestroy(ds.handle);
-      ds.handle = nullptr;
-      ds.workspace = nullptr;
-      return fail(FG_E_HIP, "hipMalloc of the %zu-byte GEMM workspace failed", WORKSPACE_BYTES);
-    }
+  if (!ds.handle) BLAS_TRY(hipblasLtCreate(&ds.handle));
+  void *&ws = ds.workspace[stream];
+  if (!ws && hipMalloc(&ws, WORKSPACE_BYTES) != hipSuccess) {
+    ws = nullptr;
+    ds.workspace.erase(stream);
+    return fail(FG_E_HIP, "hipMalloc of the %zu-byte GEMM workspace failed", WORKSPACE_BYTES);
   }
   if (ds.plans.size() >= MAX_PLANS) {  // many distinct token counts: start over
     for (auto &kv : ds.plans) destroy_plan(kv.second);
@@ -136,7 +136,7 @@ extern "C" fg_status fg_linear_bf16(const void *x, const void *w, void *y, int32
   const Plan &p = it->second;
   const float alpha = 1.f, beta = 0.f;
   BLAS_TRY(hipblasLtMatmul(ds.handle, p.desc, &alpha, w, p.a, x, p.b, &beta, y, p.d, y, p.d,
-                           &p.algo, ds.workspace, WORKSPACE_BYTES, (hipStream_t)stream));
+                           &p.algo, ws, WORKSPACE_BYTES, (hipStream_t)stream));
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_E_HIP, "GEMM launch: %s", hipGetErrorString(e));
   return FG_OK;

@@ -26,7 +26,8 @@ DTYPES = {"f32": FG_F32, "bf16": FG_BF16}
 EXPORTS = [
     "fg_blocked_cache_init", "fg_blocked_cache_destroy", "fg_blocked_cache_num_free",
     "fg_blocked_cache_free_ids", "fg_blocked_cache_release", "fg_splitfuse_compose",
-    "fg_splitfuse_commit", "fg_splitfuse_retire", "fg_validate_batch", "fg_kv_append", "fg_attention_plan",
+    "fg_splitfuse_commit", "fg_splitfuse_retire", "fg_validate_batch", "fg_validate_work",
+    "fg_kv_append", "fg_attention_plan", "fg_ragged_attention_workspace_size",
     "fg_ragged_attention", "fg_linear_bf16", "fg_status_string", "fg_last_error",
 ]
 
@@ -107,6 +108,11 @@ def _declare(L):
         "fg_splitfuse_commit": ([ctypes.POINTER(FgSeqState), ctypes.c_int32], st),
         "fg_splitfuse_retire": ([vp, ctypes.POINTER(FgSeqState), ctypes.c_int32, i32p], st),
         "fg_validate_batch": ([vp, ctypes.POINTER(FgRaggedBatch)], st),
+        "fg_validate_work": ([vp, ctypes.POINTER(FgRaggedBatch), ctypes.POINTER(FgPlanInfo), vp,
+                              ctypes.c_size_t], st),
+        "fg_ragged_attention_workspace_size": ([vp, ctypes.POINTER(FgRaggedBatch), ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
+                                               st),
         "fg_kv_append": ([vp, ctypes.POINTER(FgRaggedBatch), vp, vp, vp], st),
         "fg_attention_plan": ([vp, ctypes.POINTER(FgRaggedBatch), ctypes.c_int32, ctypes.c_int32,
                                ctypes.POINTER(FgPlanInfo), vp, ctypes.c_int32], st),
@@ -271,6 +277,21 @@ def fg_splitfuse_retire(handle, arr, n: int) -> int:
 
 def fg_validate_batch(handle, batch: HostBatch):
     _check(lib().fg_validate_batch(handle, ctypes.byref(batch.c)))
+
+
+def fg_validate_work(handle, batch: HostBatch, info: FgPlanInfo, work, workspace_bytes: int):
+    w = np.ascontiguousarray(work, dtype=np.int32)
+    _check(lib().fg_validate_work(handle, ctypes.byref(batch.c), ctypes.byref(info),
+                                  _addr(w) if w.size else None, int(workspace_bytes)))
+
+
+def fg_ragged_attention_workspace_size(handle, batch: HostBatch, num_q_heads: int,
+                                       num_cus: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().fg_ragged_attention_workspace_size(handle, ctypes.byref(batch.c),
+                                                    int(num_q_heads), int(num_cus),
+                                                    ctypes.byref(n)))
+    return int(n.value)
 
 
 def fg_attention_plan(handle, batch: HostBatch, num_q_heads: int, num_cus: int, work=None):

@@ -135,6 +135,58 @@ class ServingLoop:
         return st
 
 
+def request_latencies(stats: ServingStats, requests, pass_end_s):
+    """Per-request latencies of a served stream on a timeline of pass end times.
+
+    The effective-throughput view of serving (DeepSpeed-FastGen paper card by Holmes et al.
+    2024, "Interesting ideas": throughput that counts only requests served within a
+    first-token time and a steady token pace).  ``pass_end_s[p]`` is the time at which pass
+    p ends, on any clock whose zero is the start of pass 0.  A request joins when the pass
+    before its admission pass ends (time 0 for pass 0); its first token arrives when its
+    first-token pass ends; its later tokens arrive one per pass until its finish pass.
+    Returns two float64 arrays in ``requests`` order:
+
+    * ttft: first-token pass end - join time;
+    * pace: (finish pass end - first-token pass end) / (output_len - 1), the mean gap between
+      generated tokens; NaN for a request with a single generated token (it has no gap).
+    """
+    ends = np.asarray(pass_end_s, dtype=np.float64)
+    n = len(requests)
+    ttft, pace = np.empty(n), np.empty(n)
+    for k, r in enumerate(requests):
+        a = stats.admit_pass[r.rid]
+        f, e = stats.first_token_pass[r.rid], stats.finish_pass[r.rid]
+        join = 0.0 if a == 0 else ends[a - 1]
+        ttft[k] = ends[f] - join
+        pace[k] = (ends[e] - ends[f]) / (r.output_len - 1) if r.output_len > 1 else np.nan
+    return ttft, pace
+
+
+def sla_attainment(ttft, pace, ttft_max: float, pace_max: float) -> float:
+    """Share of requests whose first token came within ttft_max and whose token pace is within
+    pace_max (a request with one generated token has no pace and meets any pace bound)."""
+    ttft, pace = np.asarray(ttft), np.asarray(pace)
+    if ttft.size == 0:
+        return float("nan")
+    ok = (ttft <= ttft_max) & (np.isnan(pace) | (pace <= pace_max))
+    return float(ok.mean())
+
+
+def latency_summary(ttft, pace, ttft_grid=(0.5, 1.0, 2.0), pace_grid=(0.025, 0.05, 0.1)) -> dict:
+    """Mean and percentiles of TTFT and token pace (milliseconds), and SLA attainment on a grid
+    of thresholds (seconds; the pages give no thresholds, so a grid is reported)."""
+    ttft, pace = np.asarray(ttft), np.asarray(pace)
+    pc = pace[~np.isnan(pace)]
+    out = {"ttft_ms_mean": float(ttft.mean() * 1e3),
+           "ttft_ms_p50": float(np.percentile(ttft, 50) * 1e3),
+           "ttft_ms_p95": float(np.percentile(ttft, 95) * 1e3),
+           "token_pace_ms_mean": float(pc.mean() * 1e3) if pc.size else float("nan"),
+           "token_pace_ms_p95": float(np.percentile(pc, 95) * 1e3) if pc.size else float("nan")}
+    out["sla_attainment"] = {f"ttft<={a}s,pace<={b}s": sla_attainment(ttft, pace, a, b)
+                             for a in ttft_grid for b in pace_grid}
+    return out
+
+
 class Projections:
     """The dense projections of one attention layer (``fg_linear_bf16``): Q, K and V from the
     pass's hidden rows x [T][hidden] (separate weights, so each lands in the dense layout the

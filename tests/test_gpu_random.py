@@ -39,9 +39,10 @@ def draw_case(seed):
     demand = n_decode + sum(L - c for c, L in prompts)
     budget = int(rng.integers(max(1, n_decode), min(demand, 320) + 1))
     # One case in three has steep logits (spread ~8): the softmax is then nearly one-hot, so O
-    # is close to single V rows.  Values are halved there: a bf16 output carries a rounding
-    # error of up to 2^-9 |O| by itself, which reaches the 2e-2 bound once |O| > 5.12, and
-    # N(0, 1) rows drawn by the thousand reach |v| ~ 4-5.
+    # is close to single V rows.  Values are halved there (value_scale 0.5, a narrowing of the
+    # inputs, not of the bound): rounding to bf16 (unit roundoff 2^-8) carries an error of up
+    # to 2^-8 |O| by itself, which alone reaches the 2e-2 bound once |O| > 5.12, and N(0, 1)
+    # rows drawn by the thousand reach |v| ~ 4-5.
     steep = rng.random() < 1 / 3
     q_scale, value_scale = (32.0, 0.5) if steep else (1.0, 1.0)
     cus = int(rng.choice([256, 100000]))

@@ -499,3 +499,78 @@ def test_plan_reuses_a_large_enough_buffer():
     info2, work2 = fg.fg_attention_plan(h, hb, 32, 256, small)
     assert np.array_equal(work0, work2)
     fg.fg_blocked_cache_destroy(h)
+
+
+# --------------------------------------------------------------------------------------
+# work-list validation (the check FG_VALIDATE=1 runs on device copies) and workspace sizing
+# --------------------------------------------------------------------------------------
+
+def _planned(cfg=None, w=None, num_cus=256):
+    w = w or wl.make(cfg)
+    h, ss, hb = _compose_c(w)
+    info, work = fg.fg_attention_plan(h, hb, w.num_q_heads, num_cus)
+    return w, h, hb, info, np.array(work)
+
+
+def test_validate_work_accepts_every_planned_list():
+    for cfg in (2, 3, 5):
+        w, h, hb, info, work = _planned(cfg)
+        fg.fg_validate_work(h, hb, info, work, info.workspace_bytes)
+        fg.fg_blocked_cache_destroy(h)
+    # split groups present (a huge CU count forces the finest key splits)
+    w, h, hb, info, work = _planned(2, num_cus=100000)
+    assert info.num_groups > 0
+    fg.fg_validate_work(h, hb, info, work, info.workspace_bytes)
+    assert _status(fg.fg_validate_work, h, hb, info, work, info.workspace_bytes - 4) == fg.FG_E_DESC
+    fg.fg_blocked_cache_destroy(h)
+
+
+def test_validate_work_rejects_corrupted_lists():
+    """Each plausible corruption of a valid list is caught (FG_E_DESC, a named violation)."""
+    IW = fg.FG_ITEM_INTS
+    w, h, hb, info, work = _planned(2, num_cus=100000)
+    ni, hkv = info.num_items, w.num_kv_heads
+    items = lambda a: a[:ni * IW].reshape(ni, IW)
+    codes = lambda a: a[ni * IW:]
+    split_item = next(i for i in range(ni) if items(work)[i][6] >= 0 and items(work)[i][7] == 1)
+    plain_item = next(i for i in range(ni) if items(work)[i][6] < 0)
+    main = info.num_work - info.num_groups
+    first_real = next(r for r in range(main) if codes(work)[r] >= 0)
+    muts = {
+        "sequence out of range": lambda a: items(a).__setitem__((0, 0), hb.num_seqs),
+        "tokens past the sequence": lambda a: items(a).__setitem__((plain_item, 2), 10**6),
+        "unaligned key start": lambda a: items(a).__setitem__((split_item, 3), items(a)[split_item][3] + 1),
+        "keys past the row's limit": lambda a: items(a).__setitem__((plain_item, 4), items(a)[plain_item][4] + 1),
+        "keys short of the row's limit": lambda a: items(a).__setitem__((plain_item, 4), items(a)[plain_item][4] - 1),
+        "bad mode": lambda a: items(a).__setitem__((0, 5), 7),
+        "split gap": lambda a: items(a).__setitem__((split_item, 3), items(a)[split_item][3] + 64),
+        "partials outside the workspace": lambda a: items(a).__setitem__((split_item, 9), 1 << 30),
+        "record repeated": lambda a: codes(a).__setitem__(first_real + 1, codes(a)[first_real]),
+        "record out of range": lambda a: codes(a).__setitem__(first_real, ni * hkv),
+        "merge record names a plain item": lambda a: codes(a).__setitem__(main, plain_item * hkv),
+    }
+    for name, mut in muts.items():
+        bad = work.copy()
+        mut(bad)
+        assert _status(fg.fg_validate_work, h, hb, info, bad, info.workspace_bytes) == fg.FG_E_DESC, name
+        assert fg.fg_last_error(), name
+    # a plan made for another token count
+    other = fg.FgPlanInfo.from_buffer_copy(info)
+    other.num_tokens += 1
+    assert _status(fg.fg_validate_work, h, hb, other, work, info.workspace_bytes) == fg.FG_E_DESC
+    fg.fg_blocked_cache_destroy(h)
+
+
+def test_workspace_size_matches_the_plan():
+    for cfg, cus in ((2, 256), (2, 100000), (3, 256), (4, 256), (5, 256), (5, 7)):
+        w = wl.make(cfg)
+        h, ss, hb = _compose_c(w)
+        info, _ = fg.fg_attention_plan(h, hb, w.num_q_heads, cus)
+        assert fg.fg_ragged_attention_workspace_size(h, hb, w.num_q_heads, cus) == info.workspace_bytes
+        fg.fg_blocked_cache_destroy(h)
+    w = wl.make(2)
+    h, ss, hb = _compose_c(w)
+    assert _status(fg.fg_ragged_attention_workspace_size, h, hb, 31, 256) == fg.FG_E_ARG
+    n = ctypes.c_size_t(0)
+    assert fg.lib().fg_ragged_attention_workspace_size(h, ctypes.byref(hb.c), 32, 256, None) == fg.FG_E_ARG
+    fg.fg_blocked_cache_destroy(h)

@@ -201,3 +201,51 @@ def test_retire_rejects_null_arguments():
         assert n.value == 0
     finally:
         fg.fg_blocked_cache_destroy(h)
+
+
+LATENCY_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "serving_latency_hand.json")
+
+
+def test_latency_proxy_hand_timeline():
+    """The effective-throughput proxy (TTFT, token pace, SLA attainment) on the hand trace with
+    given pass times, against values worked out by hand."""
+    from ragged_blocked_kv_splitfuse_amd.serving import (latency_summary, request_latencies,
+                                                         sla_attainment)
+    g, reqs = load_hand()
+    lat = json.load(open(LATENCY_GOLDEN))
+    h = fg.fg_blocked_cache_init(len(g["free_ids"]), g["block_size"], 1, 128, "bf16", 0, 0,
+                                 np.array(g["free_ids"], np.int32))
+    try:
+        st = ServingLoop(h, g["block_size"], g["budget"], g["clients"], g["table_width"]).run(reqs)
+    finally:
+        fg.fg_blocked_cache_destroy(h)
+    assert st.passes == len(lat["pass_ms"])
+    ends = np.cumsum(np.array(lat["pass_ms"]) * 1e-3)
+    assert np.allclose(ends * 1e3, lat["pass_end_ms"])
+    ttft, pace = request_latencies(st, reqs, ends)
+    for k, r in enumerate(reqs):
+        assert ttft[k] * 1e3 == pytest.approx(lat["ttft_ms"][str(r.rid)], abs=1e-9)
+        want = lat["pace_ms"][str(r.rid)]
+        if want is None:
+            assert np.isnan(pace[k])
+        else:
+            assert pace[k] * 1e3 == pytest.approx(want, abs=1e-9)
+    for case in lat["sla"]:
+        got = sla_attainment(ttft, pace, case["ttft_ms"] * 1e-3, case["pace_ms"] * 1e-3)
+        assert got == pytest.approx(case["attainment"]), case
+    s = latency_summary(ttft, pace, ttft_grid=(0.015,), pace_grid=(0.0045,))
+    assert s["ttft_ms_mean"] == pytest.approx(9.0)
+    assert s["token_pace_ms_mean"] == pytest.approx(3.75)
+    assert s["sla_attainment"] == {"ttft<=0.015s,pace<=0.0045s": pytest.approx(1.0)}
+
+
+def test_latency_proxy_single_pass_requests():
+    """Requests served in the pass that admitted them, with one generated token: TTFT is
+    exactly that pass's duration and there is no pace."""
+    from ragged_blocked_kv_splitfuse_amd.serving import request_latencies, ServingStats
+    reqs = [W.Request(1, 3, 1), W.Request(2, 2, 1)]
+    st = ServingStats(admit_pass={1: 0, 2: 1}, first_token_pass={1: 0, 2: 1},
+                      finish_pass={1: 0, 2: 1})
+    ttft, pace = request_latencies(st, reqs, [0.25, 0.75])
+    assert ttft.tolist() == [0.25, 0.5]
+    assert np.isnan(pace).all()
