@@ -76,7 +76,7 @@ typedef struct fg_cache_config {
   int32_t block_size;   /* tokens per block: power of two in [1, 1024]; bf16 attention
                            needs >= 8 */
   int32_t num_kv_heads; /* Hkv >= 1 */
-  int32_t head_dim;     /* D: 64 or 128 for FG_F32; 128 for FG_BF16 */
+  int32_t head_dim;     /* D: 64 or 128 (both dtypes) */
   int32_t dtype;        /* fg_dtype of pools, q, k_new, v_new and out */
 } fg_cache_config;
 

@@ -73,10 +73,8 @@ fg_status fg_blocked_cache_init(const fg_cache_config *cfg, void *k_pool, void *
                 c.block_size);
   if (c.num_kv_heads < 1) return fail(FG_E_ARG, "num_kv_heads must be >= 1");
   if (c.dtype != FG_F32 && c.dtype != FG_BF16) return fail(FG_E_ARG, "unknown dtype %d", c.dtype);
-  if (c.dtype == FG_BF16 && c.head_dim != 128)
-    return fail(FG_E_UNSUPPORTED, "bf16 kernels implement head_dim 128 (got %d)", c.head_dim);
-  if (c.dtype == FG_F32 && c.head_dim != 64 && c.head_dim != 128)
-    return fail(FG_E_UNSUPPORTED, "fp32 kernels implement head_dim 64 or 128 (got %d)",
+  if (c.head_dim != 64 && c.head_dim != 128)
+    return fail(FG_E_UNSUPPORTED, "the kernels implement head_dim 64 or 128 (got %d)",
                 c.head_dim);
   if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
     return fail(FG_E_ARG, "pools must be 16-byte aligned (k_pool %p, v_pool %p)", k_pool, v_pool);

@@ -39,15 +39,15 @@ typedef uint16_t u16;
 
 namespace {
 
-constexpr int D = 128;          // head dim of the bf16 kernels
+// HD (template parameter): head dim of the bf16 kernels, 64 or 128
 constexpr int KT = KEY_TILE;    // keys per tile
 constexpr int NW = WAVES_PER_WG;  // waves per workgroup
 constexpr int NT = NW * 64;     // threads per workgroup
 // The LDS stage ring of tile records (also the stream records' merge space)
 constexpr int KS = 32;                     // keys per stage
 constexpr int NSTAGE = 4;                  // ring depth
-constexpr int STAGE_K = KS * D;            // u16 elements of the K part of a stage
-constexpr int STAGE_ELEMS = 2 * KS * D;    // K + V^T: 16 KiB
+constexpr int stage_k(int hd) { return KS * hd; }          // u16 elements of a stage's K part
+constexpr int stage_elems(int hd) { return 2 * KS * hd; }  // K + V^T: 16 KiB at HD 128
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float NEG_INF = -__builtin_inff();
 
@@ -170,6 +170,7 @@ struct Rec {
 
 // Record `idx`: its code names an item and a KV head.  A padding code, or one naming an item
 // outside the list, gives a record with s = -1 (the workgroup exits).
+template <int HD>
 __device__ __forceinline__ Rec load_rec(const Params &P, int idx) {
   Rec r;
   const int code = ldc(P.codes, idx);
@@ -191,22 +192,24 @@ __device__ __forceinline__ Rec load_rec(const Params &P, int idx) {
   r.nsplit = ldc(w, I_NSPLIT);
   const int g0 = ldc(w, I_GROUP);
   r.group = g0 >= 0 ? g0 + r.h : -1;
-  r.poff = g0 >= 0 ? ldc(w, I_POFF) + r.h * r.nsplit * (int)slot_floats(r.mode, D) : 0;
+  r.poff = g0 >= 0 ? ldc(w, I_POFF) + r.h * r.nsplit * (int)slot_floats(r.mode, HD) : 0;
   return r;
 }
 
+template <int HD>
 __device__ __forceinline__ bool rec_fits_workspace(const Params &P, const Rec &R) {
   return R.group < 0 ||
-         (int64_t)R.poff + (int64_t)R.nsplit * slot_floats(R.mode, D) <= P.ws_floats;
+         (int64_t)R.poff + (int64_t)R.nsplit * slot_floats(R.mode, HD) <= P.ws_floats;
 }
 
 // Final normalisation and bf16 store of 8 consecutive features of one query row.
+template <int HD>
 __device__ __forceinline__ void store_out8(const Params &P, int t, int head, int d0,
                                            const float *o, float inv_l) {
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = o[i] * inv_l;
-  *reinterpret_cast<bf16x8 *>(P.out + ((size_t)t * P.Hq + head) * D + d0) = to_bf16x8(v);
+  *reinterpret_cast<bf16x8 *>(P.out + ((size_t)t * P.Hq + head) * HD + d0) = to_bf16x8(v);
 }
 
 // Online softmax over one 64-key tile for one 16-row MFMA tile (FlashAttention's running
@@ -214,6 +217,7 @@ __device__ __forceinline__ void store_out8(const Params &P, int t, int head, int
 // lane's row (key0 = k0 + 8g).  The running max m lives in the scaled log2 domain; p =
 // 2^(s*scale*log2e - m).  Updates m, l (this lane's partial row sum), rescales acc when a
 // row's max moved, and returns P packed to bf16 as the B operands of the P.V product.
+template <int HD>
 __device__ __forceinline__ void online_softmax(f32x4 (&s)[2][2], bool need_mask, int key0,
                                                int lim, int khi, float sl2, float &m, float &l,
                                                f32x4 *acc, bf16x8 (&pf)[2]) {
@@ -256,19 +260,22 @@ __device__ __forceinline__ void online_softmax(f32x4 (&s)[2][2], bool need_mask,
   m = m_new;
   if (__ballot(upd)) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
+    for (int dt = 0; dt < HD / 16; ++dt) acc[dt] *= alpha;
   }
   pf[0] = to_bf16x8(p[0]);
   pf[1] = to_bf16x8(p[1]);
 }
 
-constexpr int MERGE_ROWS = NT / (D / 8);  // rows one merge workgroup covers
+constexpr int merge_rows(int hd) { return NT / (hd / 8); }  // rows one merge workgroup covers
 
 // Combine: the merge record of a split group reads every split's (m, l, acc) partial in
 // split order (deterministic) and writes O.  Runs in its own launch after the main kernel.
 // Each workgroup merges one MERGE_ROWS-row slice (blockIdx.y) of the group: one thread per (row,
 // 8-feature chunk).
+template <int HD>
 __device__ void merge_splits(const Params &P, const Rec &R) {
+  constexpr int D = HD;
+  constexpr int MERGE_ROWS = merge_rows(HD);
   const int64_t slot = slot_floats(R.mode, D);
   const int cap = R.mode == MODE_STREAM ? STREAM_ROWS : TILE_ROWS;
   const int rows = R.ntok * P.G;
@@ -291,7 +298,7 @@ __device__ void merge_splits(const Params &P, const Rec &R) {
     }
     const int t = qs + R.tok0 + row / P.G;
     const int head = R.h * P.G + row % P.G;
-    if (t < P.num_tokens) store_out8(P, t, head, chunk * 8, o, 1.f / L);
+    if (t < P.num_tokens) store_out8<HD>(P, t, head, chunk * 8, o, 1.f / L);
   }
 }
 
@@ -300,8 +307,10 @@ __device__ void merge_splits(const Params &P, const Rec &R) {
 // straight from HBM into MFMA operand registers (no LDS staging, no barriers), then the NW
 // waves merge their running states through LDS.
 // ---------------------------------------------------------------------------------------
-template <bool BIG, typename LdsT>
+template <int HD, bool BIG, typename LdsT>
 __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
+  constexpr int D = HD;
+  constexpr int STAGE_K = stage_k(HD);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
   const int c = ldc(P.context_len, R.s), qs = ldc(P.query_start, R.s);
   const int L = c + ldc(P.n_query, R.s);
@@ -419,7 +428,7 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
       }
     const bool need_mask = (k0 + KT > R.khi) || (k0 + KT - 1 > c + R.tok0);
     bf16x8 pf[2];
-    online_softmax(st, need_mask, k0 + 8 * g, lim, R.khi, P.sl2, m_run, l_run, acc, pf);
+    online_softmax<HD>(st, need_mask, k0 + 8 * g, lim, R.khi, P.sl2, m_run, l_run, acc, pf);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -443,7 +452,8 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
     sl[w * STREAM_ROWS + r] = l_run;
   }
   __syncthreads();
-  const int row = threadIdx.x >> 4, chunk = threadIdx.x & 15;  // 16 rows x 16 chunks of 8
+  // one thread per (row, 8-feature chunk); threads past row 16 have nothing to merge
+  const int row = threadIdx.x / (D / 8), chunk = threadIdx.x % (D / 8);
   if (row >= rows) return;
   float M = NEG_INF;
 #pragma unroll
@@ -460,7 +470,7 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
   }
   if (R.group < 0) {
     const int t = qs + R.tok0 + row / P.G;
-    if (t < P.num_tokens) store_out8(P, t, R.h * P.G + row % P.G, chunk * 8, o, 1.f / Lsum);
+    if (t < P.num_tokens) store_out8<HD>(P, t, R.h * P.G + row % P.G, chunk * 8, o, 1.f / Lsum);
   } else {
     float *sp = P.ws + R.poff + (int64_t)R.split * slot_floats(MODE_STREAM, D);
     *reinterpret_cast<float4 *>(sp + row * D + chunk * 8) = make_float4(o[0], o[1], o[2], o[3]);
@@ -488,16 +498,23 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
 // row's softmax state lives in two lanes (l, l^32), and all 64 accumulators of a lane belong
 // to one row, one scale factor.
 // ---------------------------------------------------------------------------------------
-static_assert(STREAM_ROWS * D * 4 <= STAGE_K * 2, "a wave's stream dump must fit a K array");
-static_assert(NW * STAGE_K <= NSTAGE * STAGE_ELEMS, "every wave's stream dump must fit the ring");
+static_assert(STREAM_ROWS * 128 * 4 <= stage_k(128) * 2 && STREAM_ROWS * 64 * 4 <= stage_k(64) * 2,
+              "a wave's stream dump must fit a K array");
+static_assert(NW * stage_k(128) <= NSTAGE * stage_elems(128) &&
+                  NW * stage_k(64) <= NSTAGE * stage_elems(64),
+              "every wave's stream dump must fit the ring");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
-// K stage: 16-byte chunk c of key row `key` sits at slot c ^ swz_k32(key).  The MFMA reads of
-// 16 lanes (rows pi(m), m = 16i .. 16i+15, one chunk) then hit 16 distinct slots.
+// K stage: 16-byte chunk c of key row `key` sits at slot c ^ swz_k32<HD>(key).  The MFMA reads
+// of 16 lanes (rows pi(m), m = 16i .. 16i+15, one chunk) then hit 16 distinct 16-byte slots of
+// a 256-byte window: at HD 128 (256-byte rows) the swizzle takes 16 values; at HD 64 (128-byte
+// rows, two per window) the row's parity picks the window half and the swizzle 8 values.
+template <int HD>
 __device__ __forceinline__ int swz_k32(int key) {
-  return (key & 3) | ((key >> 1) & 4) | ((key << 1) & 8);
+  if (HD == 128) return (key & 3) | ((key >> 1) & 4) | ((key << 1) & 8);
+  return (key >> 1) & 7;
 }
 // V^T stage: 8-key chunk kc of feature row d (64 bytes) sits at slot kc ^ swz_v32(d); 16
 // consecutive features at one chunk cover all 16 slots of a 256-byte window set.
@@ -513,11 +530,12 @@ __device__ __forceinline__ int key_perm32(int m) {
 constexpr int MAX_IDS = 256;  // block ids of a tile record staged in LDS
 static_assert(2 * NW * STREAM_ROWS <= MAX_IDS, "stream merge maxima and sums must fit");
 
+template <int HD>
 struct Lds {
   u16 *base;
   int *ids;  // MAX_IDS block ids
-  __device__ u16 *k(int i) const { return base + i * STAGE_ELEMS; }
-  __device__ u16 *v(int i) const { return base + i * STAGE_ELEMS + STAGE_K; }
+  __device__ u16 *k(int i) const { return base + i * stage_elems(HD); }
+  __device__ u16 *v(int i) const { return base + i * stage_elems(HD) + stage_k(HD); }
 };
 
 // One wave instruction: 16 bytes per lane from global memory to LDS at lds_wave_base + 16*lane.
@@ -550,88 +568,120 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// wait until at most n of this wave's LDS-DMA loads are outstanding (n even, 0 .. 16; an odd
-// or larger n waits for n rounded down)
+// wait until at most n of this wave's LDS-DMA loads are outstanding (n in 0 .. 16)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // s_waitcnt encoding (gfx9): vmcnt = bits 3:0 (+ bits 15:14), expcnt 6:4, lgkmcnt 11:8
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
+}
 __device__ __forceinline__ void wait_dma(int n) {
-  // s_waitcnt encoding (gfx9): vmcnt = bits 3:0 (+15:14), expcnt 6:4, lgkmcnt 11:8
-  if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt 16: bits 15:14 = 1, 3:0 = 0
-  else if (n >= 14) __builtin_amdgcn_s_waitcnt(0x0F70 | 14);
-  else if (n >= 12) __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
-  else if (n >= 10) __builtin_amdgcn_s_waitcnt(0x0F70 | 10);
-  else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
-  else if (n >= 6) __builtin_amdgcn_s_waitcnt(0x0F70 | 6);
-  else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
-  else if (n >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
-  else __builtin_amdgcn_s_waitcnt(0x0F70);
+  switch (n) {
+    case 0: wait_vm<0>(); break;   case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;   case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;   case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;   case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;   case 9: wait_vm<9>(); break;
+    case 10: wait_vm<10>(); break; case 11: wait_vm<11>(); break;
+    case 12: wait_vm<12>(); break; case 13: wait_vm<13>(); break;
+    case 14: wait_vm<14>(); break; case 15: wait_vm<15>(); break;
+    default: wait_vm<16>(); break;
+  }
 }
 
-// Per-lane parts of the four LDS-DMA source addresses of a stage (bytes from the stage's
-// first key in its block), constant over a record when a stage lies inside one block.
-constexpr int RPW = 8 / NW;  // 1 KiB regions of each stage half a wave fetches
+// A stage is 2 * HD / 16 regions of 1 KiB: K regions first (HD / 16 of them, key rows of 2*HD
+// bytes), then V^T regions (16 feature rows of 32 keys each).  One wave instruction fills one
+// region; wave w issues regions p * NW + w, p = 0 .. DPW - 1.
+template <int HD>
+struct Dma {
+  static constexpr int K_REGIONS = HD / 16;
+  static constexpr int DPW = 2 * K_REGIONS / NW;  // regions (instructions) per wave and stage
+  static constexpr int ROWS_PER_K_REGION = 512 / HD;
+  static_assert(DPW >= 1 && DPW * NW == 2 * K_REGIONS, "regions must split evenly over waves");
+};
+
+// Per-lane parts of a wave's LDS-DMA source addresses (bytes from the stage's first key in its
+// block), constant over a record when a stage lies inside one block.
+template <int HD>
 struct DmaOffsets {
-  uint32_t k[RPW], v[RPW];
+  uint32_t off[Dma<HD>::DPW];
   // the record's KV head in block 0 of each pool, and the bytes from one block to the next
   // (wave-uniform, so a stage's address is one scalar multiply-add away)
   const char *kh0, *vh0;
   uint64_t blk_bytes;
-  uint32_t wave_lds;  // byte offset of this wave's regions inside a stage half
 };
 
-__device__ __forceinline__ DmaOffsets dma_offsets(int bs) {
+// region g of a stage, for this lane: (is a V^T region, key row or feature row, 16-byte slot
+// in that row's source)
+template <int HD>
+__device__ __forceinline__ void dma_lane(int g, int lane, bool &isv, int &row, int &ch) {
+  constexpr int KR = Dma<HD>::K_REGIONS, RPR = Dma<HD>::ROWS_PER_K_REGION;
+  isv = g >= KR;
+  if (!isv) {  // key row, 16-byte chunk of its HD features
+    row = RPR * g + lane / (HD / 8);
+    ch = (lane % (HD / 8)) ^ swz_k32<HD>(row);
+  } else {     // feature row, 8-key chunk of its 32 keys
+    row = 16 * (g - KR) + (lane >> 2);
+    ch = (lane & 3) ^ swz_v32(row);
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ DmaOffsets<HD> dma_offsets(int bs) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  DmaOffsets o;
+  DmaOffsets<HD> o;
 #pragma unroll
-  for (int p = 0; p < RPW; ++p) {
-    const int reg = RPW * w + p;
-    // K: region `reg` holds key rows 4*reg .. 4*reg+3; lane -> (key row, 16-byte slot)
-    const int keyl = 4 * reg + (lane >> 4), ch = (lane & 15) ^ swz_k32(keyl);
-    o.k[p] = (uint32_t)(keyl * D + 8 * ch) * 2u;
-    // V^T: region `reg` holds feature rows 16*reg .. +15; lane -> (row, 8-key slot)
-    const int d = 16 * reg + (lane >> 2), kc = (lane & 3) ^ swz_v32(d);
-    o.v[p] = (uint32_t)(d * bs + 8 * kc) * 2u;
+  for (int p = 0; p < Dma<HD>::DPW; ++p) {
+    bool isv;
+    int row, ch;
+    dma_lane<HD>(p * NW + w, lane, isv, row, ch);
+    o.off[p] = isv ? (uint32_t)(row * bs + 8 * ch) * 2u : (uint32_t)(row * HD + 8 * ch) * 2u;
   }
   return o;
 }
 
 // blk: the stage's block id, read ahead by the caller (used when a stage lies in one block)
-template <int BSC>
+template <int HD, int BSC>
 __device__ __forceinline__ void issue_stage(const Params &P, const Rec &R, const int32_t *bt,
-                                            int L, int k0, int blk, const DmaOffsets &o,
-                                            u16 *buf, u16 *vbuf) {
+                                            int L, int k0, int blk, const DmaOffsets<HD> &o,
+                                            u16 *buf) {
+  constexpr int DPW = Dma<HD>::DPW, KR = Dma<HD>::K_REGIONS;
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  // wave-uniform; the mask tells the compiler w < NW, so the K/V choice of a region folds
+  // where it does not depend on the wave
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW - 1);
   const int bs_mask = P.bs - 1;
-  const size_t head_stride = (size_t)P.bs * D;
-  const uint32_t kl = lds_addr_of(buf) + o.wave_lds, vl = lds_addr_of(vbuf) + o.wave_lds;
+  const uint32_t lb = lds_addr_of(buf);
   if (BSC >= 1) {
     // a 32-key stage lies in one block: uniform base + per-lane offset
     const uint64_t hb = (uint64_t)(uint32_t)blk * o.blk_bytes;
     const uint32_t key_in_blk = (uint32_t)(k0 & bs_mask);
-    const char *kb = o.kh0 + hb + key_in_blk * (uint32_t)(D * 2);
+    const char *kb = o.kh0 + hb + key_in_blk * (uint32_t)(HD * 2);
     const char *vb = o.vh0 + hb + key_in_blk * 2u;
 #pragma unroll
-    for (int p = 0; p < RPW; ++p) dma16(reinterpret_cast<const u16 *>(kb + o.k[p]), kl + 1024u * p);
-#pragma unroll
-    for (int p = 0; p < RPW; ++p) dma16(reinterpret_cast<const u16 *>(vb + o.v[p]), vl + 1024u * p);
+    for (int p = 0; p < DPW; ++p) {
+      const int g = p * NW + w;
+      dma16(reinterpret_cast<const u16 *>((g >= KR ? vb : kb) + o.off[p]), lb + 1024u * g);
+    }
     return;
   }
+  const size_t head_stride = (size_t)P.bs * HD;
 #pragma unroll
-  for (int p = 0; p < RPW; ++p) {
-    const int reg = RPW * w + p;
-    const int keyl = 4 * reg + (lane >> 4), ch = (lane & 15) ^ swz_k32(keyl);
-    const int key = min(k0 + keyl, L - 1);
-    const int blk = clamp_block(bt[key >> P.bs_log2], P.num_blocks);
-    dma16(P.k_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)(key & bs_mask) * D + 8 * ch,
-          kl + 1024u * p);
-  }
-#pragma unroll
-  for (int p = 0; p < RPW; ++p) {
-    const int reg = RPW * w + p;
-    const int d = 16 * reg + (lane >> 2), kc = (lane & 3) ^ swz_v32(d);
-    const int key0 = min(k0 + 8 * kc, (L - 1) & ~7);
-    const int blk = clamp_block(bt[key0 >> P.bs_log2], P.num_blocks);
-    dma16(P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)d * P.bs + (key0 & bs_mask),
-          vl + 1024u * p);
+  for (int p = 0; p < DPW; ++p) {
+    const int g = p * NW + w;
+    bool isv;
+    int row, ch;
+    dma_lane<HD>(g, lane, isv, row, ch);
+    if (!isv) {
+      const int key = min(k0 + row, L - 1);
+      const int blk = clamp_block(bt[key >> P.bs_log2], P.num_blocks);
+      dma16(P.k_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)(key & bs_mask) * HD + 8 * ch,
+            lb + 1024u * g);
+    } else {
+      const int key0 = min(k0 + 8 * ch, (L - 1) & ~7);
+      const int blk = clamp_block(bt[key0 >> P.bs_log2], P.num_blocks);
+      dma16(P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)row * P.bs + (key0 & bs_mask),
+            lb + 1024u * g);
+    }
   }
 }
 
@@ -646,6 +696,7 @@ __device__ __forceinline__ void mask_t32(f32x16 &s, int key0, int lim, int khi) 
   }
 }
 
+template <int HD>
 __device__ __forceinline__ void online_softmax_t32(f32x16 &s, float sl2, float &m, float &l,
                                                    f32x16 *acc, bf16x8 (&pf)[2]) {
   float mx = s[0];
@@ -666,7 +717,7 @@ __device__ __forceinline__ void online_softmax_t32(f32x16 &s, float sl2, float &
   m = m_new;
   if (__ballot(upd)) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+    for (int dt = 0; dt < HD / 32; ++dt) acc[dt] *= alpha;
   }
   pf[0] = to_bf16x8(p);
   pf[1] = to_bf16x8(p + 8);
@@ -696,8 +747,10 @@ __device__ __forceinline__ bool softmax_t32_fast(f32x16 &s, float sl2, float m, 
   return true;
 }
 
-template <int BSC>
-__device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
+template <int HD, int BSC>
+__device__ void tile_record(const Params &P, const Rec &R, const Lds<HD> &S) {
+  constexpr int D = HD;
+  constexpr int DPW = Dma<HD>::DPW;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
   const int c = ldc(P.context_len, R.s), qs = ldc(P.query_start, R.s);
   const int L = c + ldc(P.n_query, R.s);
@@ -720,17 +773,16 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
     for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
 
   // LDS read offsets (elements) of this lane's MFMA operands within a stage
-  const int krow = key_perm32(n), kswz = n & 15;  // swz_k32(pi(n)) == n & 15
+  const int krow = key_perm32(n), kswz = swz_k32<HD>(krow);
   const int vswz = swz_v32(n);                     // swz_v32(32*dt + n) == swz_v32(n)
 
   const int s_begin = R.klo / KS, s_end = (R.khi + KS - 1) / KS, nst = s_end - s_begin;
-  DmaOffsets doff = dma_offsets(P.bs);
+  DmaOffsets<HD> doff = dma_offsets<HD>(P.bs);
   {
     const uint64_t head_bytes = (uint64_t)P.bs * D * 2;
     doff.kh0 = reinterpret_cast<const char *>(P.k_pool) + (uint64_t)R.h * head_bytes;
     doff.vh0 = reinterpret_cast<const char *>(P.v_pool) + (uint64_t)R.h * head_bytes;
     doff.blk_bytes = (uint64_t)P.Hkv * head_bytes;
-    doff.wave_lds = __builtin_amdgcn_readfirstlane(1024u * RPW * (threadIdx.x >> 6));
   }
 
   // Keys at or past khi in the last stage may hold stale bits: zero their V so they cannot
@@ -777,8 +829,8 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i)
     if (i < nst)
-      issue_stage<BSC>(P, R, bt, L, (s_begin + i) * KS,
-                       __builtin_amdgcn_readfirstlane(stage_block(i)), doff, S.k(i), S.v(i));
+      issue_stage<HD, BSC>(P, R, bt, L, (s_begin + i) * KS,
+                           __builtin_amdgcn_readfirstlane(stage_block(i)), doff, S.k(i));
   // the block id of the next stage to fetch is read one stage ahead, so that the scalar
   // load's latency never stalls the loop
   int blk_next = NSTAGE - 1 < nst ? stage_block(NSTAGE - 1) : 0;
@@ -810,11 +862,11 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
 #pragma unroll
     for (int u = 0; u < NSTAGE; ++u) {
       const int i = base + u;
-      wait_dma(2 * RPW * (NSTAGE - 2));
+      wait_dma(DPW * (NSTAGE - 2));
       stage_barrier();
-      issue_stage<BSC>(P, R, bt, L, (s_begin + i + NSTAGE - 1) * KS,
-                       __builtin_amdgcn_readfirstlane(blk_next), doff,
-                       S.k((u + NSTAGE - 1) % NSTAGE), S.v((u + NSTAGE - 1) % NSTAGE));
+      issue_stage<HD, BSC>(P, R, bt, L, (s_begin + i + NSTAGE - 1) * KS,
+                           __builtin_amdgcn_readfirstlane(blk_next), doff,
+                           S.k((u + NSTAGE - 1) % NSTAGE));
       blk_next = S.ids[(((s_begin + i + NSTAGE) * KS) >> P.bs_log2) - b_first];
       scores(S.k(u), sc);
       const u16 *Vl = S.v(u);
@@ -828,7 +880,7 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
       bf16x8 pf[2];
       if (!softmax_t32_fast(sc, P.sl2, m_run, l_run, pf)) {
         scores(S.k(u), sc);
-        online_softmax_t32(sc, P.sl2, m_run, l_run, acc, pf);
+        online_softmax_t32<HD>(sc, P.sl2, m_run, l_run, acc, pf);
       }
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
@@ -843,12 +895,12 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
       const int i = base + u;
       if (i >= nst) break;
       const int k0 = (s_begin + i) * KS;
-      wait_dma(2 * RPW * min(NSTAGE - 2, nst - 1 - i));  // this wave's loads of stage i landed
+      wait_dma(DPW * min(NSTAGE - 2, nst - 1 - i));  // this wave's loads of stage i landed
       stage_barrier();                              // ... and every other wave's
       if (i + NSTAGE - 1 < nst) {                   // refill the buffer stage i-1 used
-        issue_stage<BSC>(P, R, bt, L, (s_begin + i + NSTAGE - 1) * KS,
-                         __builtin_amdgcn_readfirstlane(blk_next), doff,
-                         S.k((u + NSTAGE - 1) % NSTAGE), S.v((u + NSTAGE - 1) % NSTAGE));
+        issue_stage<HD, BSC>(P, R, bt, L, (s_begin + i + NSTAGE - 1) * KS,
+                             __builtin_amdgcn_readfirstlane(blk_next), doff,
+                             S.k((u + NSTAGE - 1) % NSTAGE));
         if (i + NSTAGE < nst) blk_next = stage_block(i + NSTAGE);
       }
       if (k0 + KS > R.khi) zero_tail(S.v(u), k0);
@@ -871,7 +923,7 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
           // rare: recompute the scores (the stage is still in LDS) and take the full path
           scores(S.k(u), sc);
           if (need_mask) mask_t32(sc, k0 + 8 * g, lim, R.khi);
-          online_softmax_t32(sc, P.sl2, m_run, l_run, acc, pf);
+          online_softmax_t32<HD>(sc, P.sl2, m_run, l_run, acc, pf);
         }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
@@ -920,26 +972,27 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds &S) {
 // One launch serves every record of the pass: stream records (decode rows, HBM-bound) and
 // tile records (chunk rows, MFMA-bound); the branch is uniform per workgroup.
 // BSC: 0 = blocks of < 32 keys, 1 = blocks of 32 keys, 2 = blocks of >= 64 keys.
-template <int BSC>
+template <int HD, int BSC>
 __global__ __launch_bounds__(NT, WG_PER_CU) void attention_bf16_kernel(Params P) {
-  __shared__ __attribute__((aligned(16))) u16 ring[NSTAGE * STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 ring[NSTAGE * stage_elems(HD)];
   __shared__ int blk_ids[MAX_IDS];
-  const Rec R = load_rec(P, blockIdx.x);
-  if (R.s < 0 || !rec_fits_workspace(P, R)) return;  // never write outside the workspace
-  Lds S;
+  const Rec R = load_rec<HD>(P, blockIdx.x);
+  if (R.s < 0 || !rec_fits_workspace<HD>(P, R)) return;  // never write outside the workspace
+  Lds<HD> S;
   S.base = ring;
   S.ids = blk_ids;
   if (R.mode == MODE_STREAM)
-    stream_record<BSC == 2>(P, R, S);
+    stream_record<HD, BSC == 2>(P, R, S);
   else
-    tile_record<BSC>(P, R, S);
+    tile_record<HD, BSC>(P, R, S);
 }
 
 // Merge records follow the attention records in the work list, one per split group.
+template <int HD>
 __global__ __launch_bounds__(NT) void attention_combine_kernel(Params P, int32_t first) {
-  const Rec R = load_rec(P, first + blockIdx.x);
-  if (R.s < 0 || R.group < 0 || !rec_fits_workspace(P, R)) return;
-  merge_splits(P, R);
+  const Rec R = load_rec<HD>(P, first + blockIdx.x);
+  if (R.s < 0 || R.group < 0 || !rec_fits_workspace<HD>(P, R)) return;
+  merge_splits<HD>(P, R);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1082,6 +1135,27 @@ __global__ __launch_bounds__(APPEND_THREADS) void kv_append_kernel(
 }  // namespace
 
 // =======================================================================================
+// Launch of the attention records (one launch) and, when the plan splits, the merge records
+// =======================================================================================
+namespace {
+
+template <int HD>
+void launch_attention(const Params &P, int block_size, int32_t main_records, int32_t groups,
+                      hipStream_t st) {
+  if (block_size >= 64)
+    hipLaunchKernelGGL((attention_bf16_kernel<HD, 2>), dim3(main_records), dim3(NT), 0, st, P);
+  else if (block_size == 32)
+    hipLaunchKernelGGL((attention_bf16_kernel<HD, 1>), dim3(main_records), dim3(NT), 0, st, P);
+  else
+    hipLaunchKernelGGL((attention_bf16_kernel<HD, 0>), dim3(main_records), dim3(NT), 0, st, P);
+  if (groups > 0)
+    hipLaunchKernelGGL((attention_combine_kernel<HD>), dim3(groups, TILE_ROWS / merge_rows(HD)),
+                       dim3(NT), 0, st, P, main_records);
+}
+
+}  // namespace
+
+// =======================================================================================
 // Validation mode (FG_VALIDATE=1): copy the device descriptors (and work list) back on the
 // caller's stream and check them on the host before launching anything.
 // =======================================================================================
@@ -1176,7 +1250,9 @@ fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const 
     else if (tok == 32) FG_APPEND_TOK(T, HD, 32);                                             \
     else FG_APPEND_TOK(T, HD, 16);                                                            \
   } while (0)
-  if (c.dtype == FG_BF16)
+  if (c.dtype == FG_BF16 && c.head_dim == 64)
+    FG_APPEND(u16, 64);
+  else if (c.dtype == FG_BF16)
     FG_APPEND(u16, 128);
   else if (c.head_dim == 64)
     FG_APPEND(float, 64);
@@ -1251,7 +1327,8 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
     if (plan->workspace_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan->workspace_bytes))
       return fail(FG_E_WORKSPACE, "workspace of %zu bytes, plan needs %lld", workspace_bytes,
                   (long long)plan->workspace_bytes);
-    if (c.head_dim != D) return fail(FG_E_UNSUPPORTED, "bf16 head_dim %d", c.head_dim);
+    if (c.head_dim != 64 && c.head_dim != 128)
+      return fail(FG_E_UNSUPPORTED, "bf16 head_dim %d", c.head_dim);
     if (c.block_size < 8)
       return fail(FG_E_UNSUPPORTED, "bf16 attention reads 8-key runs: block_size %d < 8",
                   c.block_size);
@@ -1279,16 +1356,10 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
     P.num_blocks = c.num_blocks;
     P.sl2 = scale * LOG2E;
     const int32_t main_records = plan->num_work - plan->num_groups;
-    if (c.block_size >= 64)
-      hipLaunchKernelGGL(attention_bf16_kernel<2>, dim3(main_records), dim3(NT), 0, st, P);
-    else if (c.block_size == 32)
-      hipLaunchKernelGGL(attention_bf16_kernel<1>, dim3(main_records), dim3(NT), 0, st, P);
+    if (c.head_dim == 128)
+      launch_attention<128>(P, c.block_size, main_records, plan->num_groups, st);
     else
-      hipLaunchKernelGGL(attention_bf16_kernel<0>, dim3(main_records), dim3(NT), 0, st, P);
-    if (plan->num_groups > 0)
-      hipLaunchKernelGGL(attention_combine_kernel,
-                         dim3(plan->num_groups, TILE_ROWS / MERGE_ROWS), dim3(NT), 0, st, P,
-                         main_records);
+      launch_attention<64>(P, c.block_size, main_records, plan->num_groups, st);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_E_HIP, "attention launch: %s", hipGetErrorString(e));

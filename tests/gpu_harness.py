@@ -167,3 +167,35 @@ def compact_sub_batch(batch, seqs, k_dev, v_dev, q_rows_host, dtype):
     sub = OracleBatch(np.array(qs, np.int32), np.array(nq, np.int32), np.array(cl, np.int32),
                       bt, np.arange(len(seqs), dtype=np.int32), np.zeros(len(seqs), np.int64))
     return sub, kp, vp, np.concatenate(rows)
+
+
+def oracle_attention_by_heads(q, k_pool, v_pool, batch, num_q_heads, num_kv_heads, scale,
+                              block_size, dtype, workers=None):
+    """The oracle's attention, run on groups of KV heads in parallel threads (heads are
+    independent, so this is the oracle's own result; numpy releases the GIL in its kernels).
+    BLAS is limited to one thread per worker meanwhile."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    G = num_q_heads // num_kv_heads
+    workers = workers or max(1, min(num_kv_heads, len(os.sched_getaffinity(0)), 16))
+    groups = np.array_split(np.arange(num_kv_heads), workers)
+
+    def run(hs):
+        h0, h1 = int(hs[0]), int(hs[-1]) + 1
+        return oracle.ragged_attention(np.ascontiguousarray(q[:, h0 * G:h1 * G]),
+                                       np.ascontiguousarray(k_pool[:, h0:h1]),
+                                       np.ascontiguousarray(v_pool[:, h0:h1]), batch,
+                                       (h1 - h0) * G, h1 - h0, scale, block_size, dtype)
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1, user_api="blas")
+    except Exception:  # noqa: BLE001
+        limit = None
+    try:
+        with ThreadPoolExecutor(len(groups)) as ex:
+            parts = list(ex.map(run, [g for g in groups if len(g)]))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    return np.concatenate(parts, axis=1)

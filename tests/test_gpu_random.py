@@ -98,3 +98,32 @@ def test_random_pass_f32(seed):
     assert np.array_equal(G.to_host_bits(r["gp"].cache.k_pool, "f32").view(dt), r["k_pool"].view(dt))
     assert np.array_equal(G.to_host_bits(r["gp"].cache.v_pool, "f32").view(dt), r["v_pool"].view(dt))
     G.assert_close(G.out_to_f64(r["out"]), r["ref"], "f32", f"random_f32[{seed}]")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_pass_head_dim_64(seed):
+    """The same random draws at head dim 64 (the bf16 kernels' other head size): stream and
+    tile records, every block size, forced splits, steep logits."""
+    kw, cus = draw_case(100 + seed)
+    kw["d"] = 64
+    G.say(f"random head-dim-64 case {seed}: {kw}, num_cus {cus}")
+    w = wl.custom(71000 + seed, **kw)
+    r = G.full_pass(w, num_cus=cus)
+    dt = np.uint16
+    assert np.array_equal(G.to_host_bits(r["gp"].cache.k_pool, "bf16").view(dt), r["k_pool"].view(dt))
+    assert np.array_equal(G.to_host_bits(r["gp"].cache.v_pool, "bf16").view(dt), r["v_pool"].view(dt))
+    G.assert_close(G.out_to_f64(r["out"]), r["ref"], "bf16", f"random_hd64[{seed}]")
+
+
+@pytest.mark.parametrize("hq,hkv,bs", [(32, 32, 64), (32, 8, 64), (16, 2, 16)])
+def test_head_dim_64_mixed_pass(hq, hkv, bs):
+    """A mixed pass at head dim 64 large enough for long decode histories and several query
+    tiles per chunk, planned for the device's compute units."""
+    from ragged_blocked_kv_splitfuse_amd.runtime import num_cus
+    w = wl.custom(72000 + hq + hkv + bs, hq=hq, hkv=hkv, d=64, bs=bs, budget=1024, n_decode=12,
+                  decode_ctx=(64, 3000), prompts=((700, 1500), (0, 900)))
+    r = G.full_pass(w, num_cus=num_cus())
+    dt = np.uint16
+    assert np.array_equal(G.to_host_bits(r["gp"].cache.k_pool, "bf16").view(dt), r["k_pool"].view(dt))
+    assert np.array_equal(G.to_host_bits(r["gp"].cache.v_pool, "bf16").view(dt), r["v_pool"].view(dt))
+    G.assert_close(G.out_to_f64(r["out"]), r["ref"], "bf16", f"hd64 mixed {hq}/{hkv} bs {bs}")

@@ -177,7 +177,9 @@ def test_init_errors():
     h = ctypes.c_void_p()
     assert L.fg_blocked_cache_init(None, None, None, None, -1, ctypes.byref(h)) == fg.FG_E_ARG
     assert _status(fg.fg_blocked_cache_init, 8, 3, 1, 128, "bf16", None, None) == fg.FG_E_UNSUPPORTED
-    assert _status(fg.fg_blocked_cache_init, 8, 16, 1, 64, "bf16", None, None) == fg.FG_E_UNSUPPORTED
+    assert _status(fg.fg_blocked_cache_init, 8, 16, 1, 96, "bf16", None, None) == fg.FG_E_UNSUPPORTED
+    assert _status(fg.fg_blocked_cache_init, 8, 16, 1, 256, "bf16", None, None) == fg.FG_E_UNSUPPORTED
+    fg.fg_blocked_cache_destroy(fg.fg_blocked_cache_init(8, 16, 1, 64, "bf16", None, None))
     assert _status(fg.fg_blocked_cache_init, 8, 16, 1, 96, "f32", None, None) == fg.FG_E_UNSUPPORTED
     assert _status(fg.fg_blocked_cache_init, 8, 16, 1, 128, 7, None, None) == fg.FG_E_ARG
     assert _status(fg.fg_blocked_cache_init, 0, 16, 1, 128, "bf16", None, None) == fg.FG_E_ARG
