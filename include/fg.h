@@ -257,6 +257,27 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
                               const void *q, int32_t num_q_heads, float scale, void *out,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* fg_ragged_attention for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and the
+ * same results, bit for bit, with the split partials kept in a fixed scratch array that the
+ * library's code object holds on each device (FG_NOALLOC_WORKSPACE_BYTES per device, held
+ * until the process ends) instead of a caller workspace.  The caller still passes q, out, the
+ * device descriptors and the work list.  No device memory is allocated or freed by this call.
+ * The scratch needs no initialisation (every byte read was written earlier in the same call).
+ * Every call on a device shares that device's scratch: calls that may overlap on one device
+ * (on different streams, or from different threads without ordering) race; order them on one
+ * stream.  FG_VALIDATE is not honoured here (its copies and synchronisation are what such
+ * callers avoid); validate with fg_validate_batch / fg_validate_work on the host instead.
+ * Errors: as fg_ragged_attention; FG_E_WORKSPACE when plan->workspace_bytes exceeds
+ * FG_NOALLOC_WORKSPACE_BYTES (checked before anything else runs), FG_E_HIP if the scratch's
+ * device address cannot be looked up. */
+#define FG_NOALLOC_WORKSPACE_BYTES (64u << 20)
+fg_status fg_ragged_attention_noalloc(const fg_cache *cache, const fg_ragged_batch *dev,
+                                      const fg_attention_plan_info *plan,
+                                      const int32_t *work_dev, const void *q,
+                                      int32_t num_q_heads, float scale, void *out,
+                                      void *stream);
+
 /* ---- diagnostics -------------------------------------------------------------------- */
 /* ---- dense projections either side of attention ------------------------------------ */
 

@@ -25,6 +25,7 @@
 
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "fg_internal.h"
@@ -1265,11 +1266,15 @@ fg_status fg_kv_append(const fg_cache *cache, const fg_ragged_batch *dev, const 
   return FG_OK;
 }
 
-fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
-                              const fg_attention_plan_info *plan, const int32_t *work_dev,
-                              const void *q, int32_t num_q_heads, float scale, void *out,
-                              void *workspace, size_t workspace_bytes, void *stream) {
-  clear_error();
+}  // extern "C"
+
+namespace {
+
+// The attention call with a given workspace; `validate`: honour FG_VALIDATE.
+fg_status attention_impl(const fg_cache *cache, const fg_ragged_batch *dev,
+                         const fg_attention_plan_info *plan, const int32_t *work_dev,
+                         const void *q, int32_t num_q_heads, float scale, void *out,
+                         void *workspace, size_t workspace_bytes, void *stream, bool validate) {
   if (!cache || !dev) return fail(FG_E_ARG, "null cache or batch");
   const fg_cache_config &c = cache->cfg;
   if (num_q_heads < 1 || num_q_heads % c.num_kv_heads)
@@ -1286,7 +1291,7 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
        reinterpret_cast<uintptr_t>(workspace)) & 15)
     return fail(FG_E_ARG, "q, out and workspace must be 16-byte aligned");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (validate_mode()) {
+  if (validate && validate_mode()) {
     HostCopy h;
     fg_status r = validate_device_batch(cache, dev, st, h);
     if (r != FG_OK) return r;
@@ -1364,6 +1369,74 @@ fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FG_E_HIP, "attention launch: %s", hipGetErrorString(e));
   return FG_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// Fixed scratch for fg_ragged_attention_noalloc: the split partials live in this file-scope
+// device array instead of a caller workspace.  Each device holds its own copy (for the life
+// of the process).  Host code never passes the array's name to a kernel (on the host it is
+// only a stand-in symbol); it uses the device address hipGetSymbolAddress returns, looked up
+// once per device on the entry point's first call there.
+// ---------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[FG_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+fg_status scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FG_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(FG_E_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(FG_E_HIP, "hipGetSymbolAddress of the fixed scratch: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fg_status fg_ragged_attention(const fg_cache *cache, const fg_ragged_batch *dev,
+                              const fg_attention_plan_info *plan, const int32_t *work_dev,
+                              const void *q, int32_t num_q_heads, float scale, void *out,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  clear_error();
+  return attention_impl(cache, dev, plan, work_dev, q, num_q_heads, scale, out, workspace,
+                        workspace_bytes, stream, true);
+}
+
+fg_status fg_ragged_attention_noalloc(const fg_cache *cache, const fg_ragged_batch *dev,
+                                      const fg_attention_plan_info *plan,
+                                      const int32_t *work_dev, const void *q,
+                                      int32_t num_q_heads, float scale, void *out,
+                                      void *stream) {
+  clear_error();
+  if (plan && plan->workspace_bytes > (int64_t)FG_NOALLOC_WORKSPACE_BYTES)
+    return fail(FG_E_WORKSPACE,
+                "plan needs %lld bytes of split partials, more than the %lld-byte fixed scratch "
+                "of fg_ragged_attention_noalloc (use fg_ragged_attention with a workspace, or "
+                "plan for fewer compute units)",
+                (long long)plan->workspace_bytes, (long long)FG_NOALLOC_WORKSPACE_BYTES);
+  void *ws = nullptr;
+  if (plan && plan->workspace_bytes > 0) {
+    const fg_status r = scratch_address(&ws);
+    if (r != FG_OK) return r;
+  }
+  return attention_impl(cache, dev, plan, work_dev, q, num_q_heads, scale, out, ws,
+                        ws ? (size_t)FG_NOALLOC_WORKSPACE_BYTES : 0, stream, false);
 }
 
 }  // extern "C"

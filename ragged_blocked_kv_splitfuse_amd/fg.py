@@ -28,8 +28,10 @@ EXPORTS = [
     "fg_blocked_cache_free_ids", "fg_blocked_cache_release", "fg_splitfuse_compose",
     "fg_splitfuse_commit", "fg_splitfuse_retire", "fg_validate_batch", "fg_validate_work",
     "fg_kv_append", "fg_attention_plan", "fg_ragged_attention_workspace_size",
-    "fg_ragged_attention", "fg_linear_bf16", "fg_status_string", "fg_last_error",
+    "fg_ragged_attention", "fg_ragged_attention_noalloc", "fg_linear_bf16",
+    "fg_status_string", "fg_last_error",
 ]
+FG_NOALLOC_WORKSPACE_BYTES = 64 << 20   # include/fg.h
 
 i32p = ctypes.POINTER(ctypes.c_int32)
 i64p = ctypes.POINTER(ctypes.c_int64)
@@ -119,6 +121,9 @@ def _declare(L):
         "fg_ragged_attention": ([vp, ctypes.POINTER(FgRaggedBatch), ctypes.POINTER(FgPlanInfo),
                                  vp, vp, ctypes.c_int32, ctypes.c_float, vp, vp,
                                  ctypes.c_size_t, vp], st),
+        "fg_ragged_attention_noalloc": ([vp, ctypes.POINTER(FgRaggedBatch),
+                                         ctypes.POINTER(FgPlanInfo), vp, vp, ctypes.c_int32,
+                                         ctypes.c_float, vp, vp], st),
         "fg_linear_bf16": ([vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp], st),
         "fg_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "fg_last_error": ([], ctypes.c_char_p),
@@ -328,6 +333,13 @@ def fg_ragged_attention(handle, dev: FgRaggedBatch, info: FgPlanInfo, work_dev_p
                                      work_dev_ptr or None, q_ptr,
                                      int(num_q_heads), float(scale), out_ptr, workspace_ptr,
                                      int(workspace_bytes), stream))
+
+
+def fg_ragged_attention_noalloc(handle, dev: FgRaggedBatch, info: FgPlanInfo, work_dev_ptr,
+                                q_ptr, num_q_heads, scale, out_ptr, stream):
+    _check(lib().fg_ragged_attention_noalloc(handle, ctypes.byref(dev), ctypes.byref(info),
+                                             work_dev_ptr or None, q_ptr, int(num_q_heads),
+                                             float(scale), out_ptr, stream))
 
 
 def fg_linear_bf16(x_ptr, w_ptr, y_ptr, T, K, N, stream):

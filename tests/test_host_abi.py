@@ -576,3 +576,18 @@ def test_workspace_size_matches_the_plan():
     n = ctypes.c_size_t(0)
     assert fg.lib().fg_ragged_attention_workspace_size(h, ctypes.byref(hb.c), 32, 256, None) == fg.FG_E_ARG
     fg.fg_blocked_cache_destroy(h)
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    """The fixed-scratch attention refuses a plan whose split partials exceed the scratch,
+    before any device call (so this runs without a GPU)."""
+    h = fg.fg_blocked_cache_init(8, 64, 1, 128, "bf16", 0x1000, 0x2000)
+    dev = fg.FgRaggedBatch()
+    dev.num_seqs, dev.num_tokens = 1, 4
+    info = fg.FgPlanInfo()
+    info.workspace_bytes = fg.FG_NOALLOC_WORKSPACE_BYTES + 1
+    info.num_q_heads, info.num_tokens = 1, 4
+    assert _status(fg.fg_ragged_attention_noalloc, h, dev, info, 0x7000, 0x4000, 1, 1.0, 0x5000,
+                   None) == fg.FG_E_WORKSPACE
+    assert "scratch" in fg.fg_last_error()
+    fg.fg_blocked_cache_destroy(h)
