@@ -33,11 +33,16 @@
  * Data layouts (element type = the cache dtype everywhere: float or bfloat16 bits):
  *   q, out        [T][Hq][D]        T = batch num_tokens, rows in batch order
  *   k_new, v_new  [T][Hkv][D]
- *   K pool        [num_blocks][Hkv][block_size][D]   key-major inside a block
- *   V pool        [num_blocks][Hkv][D][block_size]   feature-major inside a block
- * The V pool keeps each block feature-major so that the P.V contraction, which runs over
- * keys, reads keys contiguously; the K pool keeps keys major so that Q.K^T, which runs over
- * the head dimension, reads D contiguously.  Query head g uses KV head g / (Hq / Hkv).
+ *   K pool        [num_blocks][Hkv][block_size][D]          key-major inside a block
+ *   V pool        [num_blocks][Hkv][block_size/g][D][g]     g = min(8, block_size): slots in
+ *                                                          groups of g, each group
+ *                                                          feature-major, its g slots adjacent
+ * Slot s of a block holds its key's K row at K[b][h][s][:] and V row at V[b][h][s/g][:][s%g].
+ * The K pool keeps keys major so that Q.K^T, which runs over the head dimension, reads D
+ * contiguously.  The P.V contraction runs over keys, so each V feature keeps 8 consecutive
+ * keys adjacent (one 16-byte bf16 operand load), while a single key's V row still spans only
+ * 16*D bytes (16 cache lines at D = 128), which keeps the append of a decode token cheap.
+ * Query head g uses KV head g / (Hq / Hkv).
  */
 #ifndef FG_H
 #define FG_H

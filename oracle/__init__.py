@@ -41,10 +41,12 @@ from .bf16 import bf16_bits_to_f64
 from .compose import FreeList, OracleBatch, SeqState, splitfuse_compose, commit_pass
 from .append import kv_append
 from .attention import ragged_attention
+from .layout import k_pool_shape, v_pool_shape, v_slot
 from .linear import linear
 from .serving import serve
 
 __all__ = [
     "bf16_bits_to_f64", "FreeList", "OracleBatch", "SeqState", "splitfuse_compose",
-    "commit_pass", "kv_append", "ragged_attention", "linear", "serve",
+    "commit_pass", "kv_append", "ragged_attention", "linear", "serve", "k_pool_shape",
+    "v_pool_shape", "v_slot",
 ]

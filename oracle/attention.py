@@ -13,7 +13,8 @@ which pass computes a row.  So the oracle is the plain definition:
         o   = sum_j exp(l_j - max l) v_j / sum_j exp(l_j - max l)
 
 Keys are gathered through the block table (position j -> block
-``block_table[s][j // bs]``, slot ``j % bs``), widened exactly to float64.
+``block_table[s][j // bs]``, slot ``j % bs``; the V pool keeps slots in groups
+of min(8, bs), see ``layout``), widened exactly to float64.
 Readings where the pages are silent: the new rows are appended before the
 pass attends (a query sees its own chunk's earlier rows and itself);
 contiguous GQA groups; ``scale`` is an argument (1/sqrt(D) in every workload).
@@ -34,10 +35,11 @@ def gather_history(k_pool, v_pool, table_row, length, block_size, dtype):
     if nb and blocks.min() < 0:
         raise ValueError("history position has no block")
     K = to_f64(k_pool[blocks], dtype)                      # [nb][Hkv][bs][D]
-    V = to_f64(v_pool[blocks], dtype)                      # [nb][Hkv][D][bs]
+    V = to_f64(v_pool[blocks], dtype)                      # [nb][Hkv][bs/g][D][g]
     hkv, d = K.shape[1], K.shape[3]
     K = K.transpose(1, 0, 2, 3).reshape(hkv, nb * block_size, d)[:, :length]
-    V = V.transpose(1, 0, 3, 2).reshape(hkv, nb * block_size, d)[:, :length]
+    # key (block, group, index in group) -> position block*bs + group*g + index
+    V = V.transpose(1, 0, 2, 4, 3).reshape(hkv, nb * block_size, d)[:, :length]
     return K, V
 
 

@@ -19,7 +19,8 @@
 // l own eight *consecutive* keys (8*(l/16) .. +7) of a 32-key half tile for its row — exactly
 // the B operand layout of the second product O^T = V^T . P^T (k = 32 keys).  P therefore
 // never leaves registers, and the A operand V^T needs eight consecutive keys of one feature,
-// which the feature-major V block layout provides as one 16-byte load.
+// which the V pool layout (keys in groups of 8, each group feature-major with its 8 keys
+// adjacent) provides as one 16-byte load.
 
 #include <hip/hip_runtime.h>
 
@@ -389,10 +390,9 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
         for (int dc = 0; dc < D / 32; ++dc) kf[kh][a][dc] = as_bf16x8(ld16(kp + 32 * dc));
       }
     // ---- V^T operand: 8 consecutive keys of one feature per lane ------------------------
-    // A feature row of a V block is one 128-byte line at blocks of 64 keys; the two key
-    // halves (kh) read its two 64-byte halves.  They are requested by consecutive
-    // instructions, so that the second finds the line still in flight or cached: requested
-    // 8 instructions apart, a line is sometimes evicted in between and fetched again.
+    // In a block, V is stored as groups of 8 keys, each group feature-major with its 8 keys
+    // adjacent (16 bytes).  One instruction (fixed kh, dt) reads, for each of the four lane
+    // groups g, 16 consecutive features of one key group: four contiguous 256-byte runs.
     uint4 vr[2][D / 16];
     const u16 *vp[2];
 #pragma unroll
@@ -402,13 +402,13 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
         keyc = v_key(k0, kh);
         blk = blk_v[kh];
       }
-      vp[kh] = P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (keyc & bs_mask) +
-               (size_t)r * P.bs;
+      vp[kh] = P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride +
+               (size_t)(((keyc & bs_mask) >> 3) * D + r) * 8;
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) vr[kh][dt] = ld16(vp[kh] + (size_t)16 * dt * P.bs);
+      for (int kh = 0; kh < 2; ++kh) vr[kh][dt] = ld16(vp[kh] + 128 * dt);
     if (k0 + KT > R.khi) {  // keys at or past khi: zero V so stale bits cannot reach O
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
@@ -517,16 +517,16 @@ __device__ __forceinline__ int swz_k32(int key) {
   if (HD == 128) return (key & 3) | ((key >> 1) & 4) | ((key << 1) & 8);
   return (key >> 1) & 7;
 }
-// V^T stage: 8-key chunk kc of feature row d (64 bytes) sits at slot kc ^ swz_v32(d); 16
-// consecutive features at one chunk cover all 16 slots of a 256-byte window set.
-__device__ __forceinline__ int swz_v32(int d) { return (d >> 2) & 3; }
+// V stage: the pool's own layout, [4 key groups][HD features][8 keys]: 16 lanes reading 16
+// consecutive features of one key group read 256 contiguous bytes, so the operand reads are
+// free of bank conflicts without a swizzle.
 // pi: A row m of the score product reads physical key pi(m) of the stage (an involution)
 __device__ __forceinline__ int key_perm32(int m) {
   return (m & ~12) | ((m >> 1) & 4) | ((m << 1) & 8);
 }
 
-// The stage ring: one workgroup-shared array, stage buffer i = K [32 keys][128] followed by
-// V^T [128][32 keys].  Buffers are addressed as base + constant offset, so one set of per-lane
+// The stage ring: one workgroup-shared array, stage buffer i = K [32 keys][HD] followed by
+// V [4 key groups][HD][8 keys].  Buffers are addressed as base + constant offset, so one set of per-lane
 // address registers serves every buffer.
 constexpr int MAX_IDS = 256;  // block ids of a tile record staged in LDS
 static_assert(2 * NW * STREAM_ROWS <= MAX_IDS, "stream merge maxima and sums must fit");
@@ -590,8 +590,9 @@ __device__ __forceinline__ void wait_dma(int n) {
 }
 
 // A stage is 2 * HD / 16 regions of 1 KiB: K regions first (HD / 16 of them, key rows of 2*HD
-// bytes), then V^T regions (16 feature rows of 32 keys each).  One wave instruction fills one
-// region; wave w issues regions p * NW + w, p = 0 .. DPW - 1.
+// bytes), then V regions (64 consecutive 16-byte (key group, feature) runs each: the stage's V
+// is one contiguous piece of its block).  One wave instruction fills one region; wave w issues
+// regions p * NW + w, p = 0 .. DPW - 1.
 template <int HD>
 struct Dma {
   static constexpr int K_REGIONS = HD / 16;
@@ -611,18 +612,19 @@ struct DmaOffsets {
   uint64_t blk_bytes;
 };
 
-// region g of a stage, for this lane: (is a V^T region, key row or feature row, 16-byte slot
-// in that row's source)
+// region g of a stage, for this lane: a K region gives (key row, 16-byte chunk of its HD
+// features); a V region gives (key group, feature) of the lane's 16-byte run
 template <int HD>
 __device__ __forceinline__ void dma_lane(int g, int lane, bool &isv, int &row, int &ch) {
   constexpr int KR = Dma<HD>::K_REGIONS, RPR = Dma<HD>::ROWS_PER_K_REGION;
   isv = g >= KR;
-  if (!isv) {  // key row, 16-byte chunk of its HD features
+  if (!isv) {
     row = RPR * g + lane / (HD / 8);
     ch = (lane % (HD / 8)) ^ swz_k32<HD>(row);
-  } else {     // feature row, 8-key chunk of its 32 keys
-    row = 16 * (g - KR) + (lane >> 2);
-    ch = (lane & 3) ^ swz_v32(row);
+  } else {
+    const int unit = 64 * (g - KR) + lane;
+    row = unit / HD;   // key group of the stage (0 .. 3)
+    ch = unit % HD;    // feature
   }
 }
 
@@ -635,7 +637,7 @@ __device__ __forceinline__ DmaOffsets<HD> dma_offsets(int bs) {
     bool isv;
     int row, ch;
     dma_lane<HD>(p * NW + w, lane, isv, row, ch);
-    o.off[p] = isv ? (uint32_t)(row * bs + 8 * ch) * 2u : (uint32_t)(row * HD + 8 * ch) * 2u;
+    o.off[p] = isv ? (uint32_t)(row * HD + ch) * 16u : (uint32_t)(row * HD + 8 * ch) * 2u;
   }
   return o;
 }
@@ -657,7 +659,7 @@ __device__ __forceinline__ void issue_stage(const Params &P, const Rec &R, const
     const uint64_t hb = (uint64_t)(uint32_t)blk * o.blk_bytes;
     const uint32_t key_in_blk = (uint32_t)(k0 & bs_mask);
     const char *kb = o.kh0 + hb + key_in_blk * (uint32_t)(HD * 2);
-    const char *vb = o.vh0 + hb + key_in_blk * 2u;
+    const char *vb = o.vh0 + hb + key_in_blk * (uint32_t)(HD * 2);  // 8-key groups of 16*HD bytes
 #pragma unroll
     for (int p = 0; p < DPW; ++p) {
       const int g = p * NW + w;
@@ -678,9 +680,10 @@ __device__ __forceinline__ void issue_stage(const Params &P, const Rec &R, const
       dma16(P.k_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)(key & bs_mask) * HD + 8 * ch,
             lb + 1024u * g);
     } else {
-      const int key0 = min(k0 + 8 * ch, (L - 1) & ~7);
+      const int key0 = min(k0 + 8 * row, (L - 1) & ~7);
       const int blk = clamp_block(bt[key0 >> P.bs_log2], P.num_blocks);
-      dma16(P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride + (size_t)row * P.bs + (key0 & bs_mask),
+      dma16(P.v_pool + ((size_t)blk * P.Hkv + R.h) * head_stride +
+                (size_t)(((key0 & bs_mask) >> 3) * HD + ch) * 8,
             lb + 1024u * g);
     }
   }
@@ -775,7 +778,6 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds<HD> &S) {
 
   // LDS read offsets (elements) of this lane's MFMA operands within a stage
   const int krow = key_perm32(n), kswz = swz_k32<HD>(krow);
-  const int vswz = swz_v32(n);                     // swz_v32(32*dt + n) == swz_v32(n)
 
   const int s_begin = R.klo / KS, s_end = (R.khi + KS - 1) / KS, nst = s_end - s_begin;
   DmaOffsets<HD> doff = dma_offsets<HD>(P.bs);
@@ -791,7 +793,7 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds<HD> &S) {
   auto zero_tail = [&](u16 *Vl, int k0) {
     for (int idx = tid; idx < D * KS; idx += NT) {
       const int d = idx / KS, key = idx % KS;
-      if (k0 + key >= R.khi) Vl[d * KS + 8 * ((key >> 3) ^ swz_v32(d)) + (key & 7)] = 0;
+      if (k0 + key >= R.khi) Vl[((key >> 3) * D + d) * 8 + (key & 7)] = 0;
     }
     __syncthreads();
   };
@@ -877,7 +879,7 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds<HD> &S) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           vf[dt][h] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-              Vl + (32 * dt + n) * KS + 8 * ((2 * h + g) ^ vswz)));
+              Vl + ((2 * h + g) * D + 32 * dt + n) * 8));
       bf16x8 pf[2];
       if (!softmax_t32_fast(sc, P.sl2, m_run, l_run, pf)) {
         scores(S.k(u), sc);
@@ -909,14 +911,14 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds<HD> &S) {
       if (active && k0 <= wave_hi) {
         scores(S.k(u), sc);
         const u16 *Vl = S.v(u);
-        // V^T operands: feature 32*dt + n, keys 16*h + 8*g .. +7
+        // V^T operands: feature 32*dt + n, keys 16*h + 8*g .. +7 (key group 2*h + g)
         bf16x8 vf[D / 32][2];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int h = 0; h < 2; ++h)
             vf[dt][h] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                Vl + (32 * dt + n) * KS + 8 * ((2 * h + g) ^ vswz)));
+                Vl + ((2 * h + g) * D + 32 * dt + n) * 8));
         const bool need_mask = (k0 + KS > R.khi) || (k0 + KS - 1 > wave_lo);
         if (need_mask) mask_t32(sc, k0 + 8 * g, lim, R.khi);
         bf16x8 pf[2];
@@ -1008,6 +1010,7 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(
     const float *__restrict__ v_pool, float *__restrict__ out, int32_t Hq, int32_t Hkv,
     int32_t bs, int32_t bs_log2, int32_t num_blocks, float scale) {
   __shared__ float sq[HD];
+  const int vgl = min(bs_log2, 3);  // V slots in groups of min(8, bs)
   const int t = blockIdx.x / Hq, gq = blockIdx.x % Hq, lane = threadIdx.x;
   int lo = 0, hi = num_seqs;  // find s with query_start[s] <= t < query_start[s+1]
   while (hi - lo > 1) {
@@ -1052,9 +1055,11 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(
       const float pj = __shfl(p, j, 64);
       const int kk = k0 + j;
       const int blk = clamp_block(bt[kk >> bs_log2], num_blocks);
-      const float *vp = v_pool + ((size_t)blk * Hkv + h) * HD * bs + (kk & (bs - 1));
+      const int slot = kk & (bs - 1);
+      const float *vp = v_pool + ((size_t)blk * Hkv + h) * HD * bs +
+                        ((size_t)((slot >> vgl) * HD) << vgl) + (slot & ((1 << vgl) - 1));
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(pj, vp[(size_t)(lane + 64 * i) * bs], acc[i]);
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(pj, vp[(size_t)(lane + 64 * i) << vgl], acc[i]);
     }
   }
 #pragma unroll
@@ -1063,9 +1068,10 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(
 
 // ---------------------------------------------------------------------------------------
 // KV append: one workgroup per (tile of TOK consecutive new tokens, KV head).  K rows are
-// copied whole in 16-byte chunks (a K block row is contiguous).  V rows are staged in LDS
-// and written feature by feature with lanes on consecutive tokens, so the tokens of a prompt
-// chunk that share a block fill consecutive slots of each feature row (coalesced stores).
+// copied whole in 16-byte chunks (a K block row is contiguous).  V rows are staged in LDS and
+// written as 8 tokens x 8 features per wave instruction: in the V layout (groups of 8 slots,
+// each feature's 8 slots adjacent) the 8 consecutive tokens of a prompt chunk fill one group's
+// 8 features as one 128-byte line, and a lone decode token's row touches 16 lines in all.
 // TOK is 64, 32 or 16: the largest that still gives APPEND_MIN_WGS workgroups, so that a
 // small pass (a few hundred decode tokens, or a 512-token chunk) still spreads over the chip.
 // ---------------------------------------------------------------------------------------
@@ -1125,12 +1131,17 @@ __global__ __launch_bounds__(APPEND_THREADS) void kv_append_kernel(
     dst[3] = v.w;
   }
   __syncthreads();
-  const int tok = tid % TOK;
-  const int blk = dblk[tok];
-  if (blk < 0) return;
-  T *vrow = v_pool + ((size_t)blk * Hkv + h) * HD * bs + dslot[tok];
-  for (int d = tid / TOK; d < HD; d += APPEND_THREADS / TOK)
-    vrow[(size_t)d * bs] = vt[tok * ROWP + d];
+  const int vgl = min(bs_log2, 3);  // V slots in groups of min(8, bs)
+  for (int idx = tid; idx < TOK * HD; idx += APPEND_THREADS) {
+    const int u = idx >> 6, within = idx & 63;
+    const int tok = 8 * (u % (TOK / 8)) + (within & 7);
+    const int d = 8 * (u / (TOK / 8)) + (within >> 3);
+    const int blk = dblk[tok];
+    if (blk < 0) continue;
+    const int slot = dslot[tok];
+    v_pool[((size_t)blk * Hkv + h) * HD * bs + ((size_t)((slot >> vgl) * HD + d) << vgl) +
+           (slot & ((1 << vgl) - 1))] = vt[tok * ROWP + d];
+  }
 }
 
 }  // namespace

@@ -31,23 +31,35 @@ def stream_handle(stream=None) -> int:
     return int(s.cuda_stream)
 
 
+def v_group(block_size: int) -> int:
+    """Keys per group of the V pool layout (include/fg.h): min(8, block_size)."""
+    return min(8, int(block_size))
+
+
+def pool_shapes(num_blocks, block_size, num_kv_heads, head_dim):
+    """(K pool shape, V pool shape) of the layout include/fg.h declares."""
+    g = v_group(block_size)
+    return ((num_blocks, num_kv_heads, block_size, head_dim),
+            (num_blocks, num_kv_heads, block_size // g, head_dim, g))
+
+
 class PagedKVCache:
-    """Pools: K [NB][Hkv][bs][D], V [NB][Hkv][D][bs] in the cache dtype."""
+    """Pools: K [NB][Hkv][bs][D], V [NB][Hkv][bs/g][D][g] (g = min(8, bs)) in the cache
+    dtype."""
 
     def __init__(self, num_blocks, block_size, num_kv_heads, head_dim, dtype, device="cuda",
                  free_ids=None, k_pool=None, v_pool=None):
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
         self.num_kv_heads, self.head_dim, self.dtype = int(num_kv_heads), int(head_dim), dtype
         tdt = TORCH_DTYPES[dtype]
+        ks, vs = pool_shapes(self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
         if k_pool is None:
-            k_pool = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=tdt,
-                                 device=device)
+            k_pool = torch.empty(ks, dtype=tdt, device=device)
         if v_pool is None:
-            v_pool = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=tdt,
-                                 device=device)
+            v_pool = torch.empty(vs, dtype=tdt, device=device)
         assert k_pool.is_contiguous() and v_pool.is_contiguous()
-        assert tuple(k_pool.shape) == (num_blocks, num_kv_heads, block_size, head_dim)
-        assert tuple(v_pool.shape) == (num_blocks, num_kv_heads, head_dim, block_size)
+        assert tuple(k_pool.shape) == ks, (tuple(k_pool.shape), ks)
+        assert tuple(v_pool.shape) == vs, (tuple(v_pool.shape), vs)
         assert k_pool.dtype == tdt and v_pool.dtype == tdt
         self.k_pool, self.v_pool = k_pool, v_pool
         self.handle = fg.fg_blocked_cache_init(num_blocks, block_size, num_kv_heads, head_dim,

@@ -13,13 +13,14 @@ SENT_F32 = np.uint32(0x7FC00001)
 
 
 def empty_pools(w):
-    NB, H, bs, D = w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
+    ks = oracle.k_pool_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size)
+    vs = oracle.v_pool_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size)
     if w.dtype == "bf16":
-        k = np.full((NB, H, bs, D), SENT_BF16, np.uint16)
-        v = np.full((NB, H, D, bs), SENT_BF16, np.uint16)
+        k = np.full(ks, SENT_BF16, np.uint16)
+        v = np.full(vs, SENT_BF16, np.uint16)
     else:
-        k = np.full((NB, H, bs, D), SENT_F32, np.uint32).view(np.float32)
-        v = np.full((NB, H, D, bs), SENT_F32, np.uint32).view(np.float32)
+        k = np.full(ks, SENT_F32, np.uint32).view(np.float32)
+        v = np.full(vs, SENT_F32, np.uint32).view(np.float32)
     return k, v
 
 

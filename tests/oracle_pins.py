@@ -120,8 +120,9 @@ def check_golden_attention(attn, append):
     g = _golden_attention()
     NB, bs, D = g["num_blocks"], g["block_size"], g["head_dim"]
     sent = np.uint32(0x7FC00001)
+    g8 = min(8, bs)        # V slots in groups of min(8, bs), feature-major in a group
     k_pool = np.full((NB, 1, bs, D), sent, np.uint32).view(np.float32)
-    v_pool = np.full((NB, 1, D, bs), sent, np.uint32).view(np.float32)
+    v_pool = np.full((NB, 1, bs // g8, D, g8), sent, np.uint32).view(np.float32)
     rows_k = np.array(g["k_rows"], np.float32)[:, None, :]
     rows_v = np.array(g["v_rows"], np.float32)[:, None, :]
     c, n = g["context_len"], g["n_new"]
@@ -140,14 +141,14 @@ def check_golden_attention(attn, append):
             return float("inf")
     for key, val in g["expected_v_slots"].items():
         b, s = map(int, key.split(","))
-        if not np.allclose(v_pool[b, 0, :, s], val, atol=0, rtol=1e-7):
+        if not np.allclose(v_pool[b, 0, s // g8, :, s % g8], val, atol=0, rtol=1e-7):
             return float("inf")
     touched = {tuple(map(int, k.split(","))) for k in g["expected_k_slots"]}
     for b in range(NB):
         for s in range(bs):
             if (b, s) not in touched:
                 if not (np.all(k_pool[b, 0, s, :].view(np.uint32) == sent)
-                        and np.all(v_pool[b, 0, :, s].view(np.uint32) == sent)):
+                        and np.all(v_pool[b, 0, s // g8, :, s % g8].view(np.uint32) == sent)):
                     return float("inf")
     q = np.array(g["q_rows"], np.float32)[:, None, :]
     out = attn(q, k_pool, v_pool, batch, 1, 1, g["scale"], bs, "f32")
@@ -163,14 +164,15 @@ def _one_seq_batch(c, n, table):
 def _pool_from_rows(K, V, table, bs, NB):
     """Place contiguous rows [L][H][D] into fp32 pools by hand (block-major loops)."""
     L, H, D = K.shape
+    g8 = min(8, bs)        # V slots in groups of min(8, bs), feature-major in a group
     kp = np.full((NB, H, bs, D), np.nan, np.float32)
-    vp = np.full((NB, H, D, bs), np.nan, np.float32)
+    vp = np.full((NB, H, bs // g8, D, g8), np.nan, np.float32)
     for p in range(L):
         b = table[p // bs]
         for h in range(H):
             for d in range(D):
                 kp[b, h, p % bs, d] = K[p, h, d]
-                vp[b, h, d, p % bs] = V[p, h, d]
+                vp[b, h, (p % bs) // g8, d, (p % bs) % g8] = V[p, h, d]
     return kp, vp
 
 

@@ -54,10 +54,10 @@ def test_decode_only_32_sequences():
 def test_decode_only_full_size():
     w = wl.make(3)
     G.say(f"decode_only full: {w.num_blocks} blocks, pools {2 * w.num_blocks * 2**20 / 2**30:.1f} GiB")
-    kp = torch.empty((w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim), dtype=torch.bfloat16,
-                     device="cuda")
-    vp = torch.empty((w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size), dtype=torch.bfloat16,
-                     device="cuda")
+    kp = torch.empty(oracle.k_pool_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size),
+                     dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty(oracle.v_pool_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size),
+                     dtype=torch.bfloat16, device="cuda")
     wl.fill_pools_device(kp, vp, seed=31337)
     k_before, v_before = kp.clone(), vp.clone()
     gp = G.GpuPass(w, kp, vp, num_cus=num_cus())
@@ -77,15 +77,17 @@ def test_decode_only_full_size():
     pos = ob.context_len.astype(np.int64)               # each entry has one new token here
     blk = ob.block_table[np.arange(T), pos // bs].astype(np.int64)
     slot = pos % bs
+    grp, j = oracle.v_slot(bs, slot)
     bi = torch.from_numpy(blk).cuda()
     si = torch.from_numpy(slot).cuda()
+    gi, ji = torch.from_numpy(grp).cuda(), torch.from_numpy(j).cuda()
     assert torch.equal(kp[bi, :, si, :].view(torch.int16), knd.view(torch.int16))
-    assert torch.equal(vp[bi, :, :, si].view(torch.int16), vnd.view(torch.int16))
+    assert torch.equal(vp[bi, :, gi, :, ji].view(torch.int16), vnd.view(torch.int16))
     changed_k = int((kp.view(torch.int16) != k_before.view(torch.int16)).sum())
     changed_v = int((vp.view(torch.int16) != v_before.view(torch.int16)).sum())
     kp_fix, vp_fix = k_before.clone(), v_before.clone()
     kp_fix[bi, :, si, :] = knd
-    vp_fix[bi, :, :, si] = vnd
+    vp_fix[bi, :, gi, :, ji] = vnd
     assert torch.equal(kp_fix.view(torch.int16), kp.view(torch.int16))
     assert torch.equal(vp_fix.view(torch.int16), vp.view(torch.int16))
     G.say(f"append: {changed_k} K and {changed_v} V elements changed, all at new slots")

@@ -24,7 +24,8 @@ def unpaged_reference(v, rid, c, n):
     K = v.k_rows(rid, 0, nb * bs)                       # [nb*bs][Hkv][D]
     V = v.v_rows(rid, 0, nb * bs)
     kp = K.reshape(nb, bs, v.num_kv_heads, v.head_dim).transpose(0, 2, 1, 3).copy()
-    vp = V.reshape(nb, bs, v.num_kv_heads, v.head_dim).transpose(0, 2, 3, 1).copy()
+    g = min(8, bs)   # the V layout: slots in groups of min(8, bs), feature-major in a group
+    vp = V.reshape(nb, bs // g, g, v.num_kv_heads, v.head_dim).transpose(0, 3, 1, 4, 2).copy()
     b = OracleBatch(np.array([0, n], np.int32), np.array([n], np.int32), np.array([c], np.int32),
                     np.arange(nb, dtype=np.int32)[None, :], np.zeros(1, np.int32),
                     np.array([rid], np.int64))

@@ -8,6 +8,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import gpu_harness as G
+import oracle
 from ragged_blocked_kv_splitfuse_amd import fg, workloads as wl
 from ragged_blocked_kv_splitfuse_amd.runtime import stream_handle
 
@@ -45,8 +46,8 @@ def test_corrupted_descriptors_rejected(monkeypatch):
     monkeypatch.setenv("FG_VALIDATE", "1")
     w = _workload()
     kp0, vp0 = (torch.full(s, 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-                for s in ((w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim),
-                          (w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size)))
+                for s in (oracle.k_pool_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size),
+                          oracle.v_pool_shape(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size)))
     gp = G.GpuPass(w, kp0, vp0, num_cus=100000)
     hb = gp.compose()
     info, work = fg.fg_attention_plan(gp.cache.handle, hb, w.num_q_heads, gp.num_cus)

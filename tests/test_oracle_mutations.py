@@ -58,7 +58,7 @@ ATTN_MUTATIONS = [
     ("keys <= c + rows", "keys <= rows"),                    # causal offset ignores the context
     (") * scale", ")"),                                      # scale dropped
     ("h = g // group", "h = g % num_kv_heads"),              # interleaved GQA groups
-    ("V.transpose(1, 0, 3, 2)", "V.transpose(1, 0, 2, 3)"),  # V read key-major
+    ("V.transpose(1, 0, 2, 4, 3)", "V.transpose(1, 0, 2, 3, 4)"),  # V group read key-major
     ("w.sum(axis=1, keepdims=True)", "w.sum()"),             # wrong normaliser
     ("visible = c + i1", "visible = c + i1 - 1"),            # last key dropped
     ("blocks = np.asarray(table_row[:nb]", "blocks = np.asarray(table_row[1:nb + 1]"),
@@ -75,7 +75,8 @@ def test_attention_mutation_caught(old, new):
 APPEND_MUTATIONS = [
     ("slot = p % block_size", "slot = (p + 1) % block_size"),
     ("p = c + i", "p = i"),
-    ("v_pool[blk, :, :, slot]", "v_pool[blk, :, slot, :]"),
+    ("v_pool[blk, :, grp, :, j]", "v_pool[blk, :, j % v_pool.shape[2], :, grp % v_pool.shape[4]]"),
+    ("grp, j = v_slot(block_size, slot)", "grp, j = v_slot(block_size, slot)[::-1]"),
     ("block_table[s, p // block_size]", "block_table[s, p % block_size]"),
 ]
 
