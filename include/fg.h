@@ -19,11 +19,8 @@
  *     new K/V, outputs, device copies of descriptors, the work list and the workspace.  The
  *     library owns only the opaque fg_cache handle and its free list (host memory).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
- *     enqueued asynchronously on it.  No entry point of the pass (fg_kv_append,
- *     fg_ragged_attention and their helpers) allocates device memory or synchronises, except
- *     in validation mode (FG_VALIDATE=1, see fg_kv_append); the
- *     one exception in this header is fg_linear_bf16, which creates its GEMM library handle
- *     and a scratch buffer on first use (see there).
+ *     enqueued asynchronously on it.  No entry point allocates device memory or
+ *     synchronises, except in validation mode (FG_VALIDATE=1, see fg_kv_append).
  *   - Every function returns fg_status and never aborts or throws across the ABI.  On an
  *     error nothing is launched and no state is changed, unless stated otherwise;
  *     fg_last_error() returns a thread-local message for the last failing call.
@@ -290,13 +287,11 @@ fg_status fg_ragged_attention_noalloc(const fg_cache *cache, const fg_ragged_bat
  * FlashAttention and FasterTransformer): the QKV projection whose K and V rows feed
  * fg_kv_append and whose Q rows feed fg_ragged_attention, and the output projection of the
  * attention rows.  y[T][N] = x[T][K] . w[N][K]^T (w in the [out][in] layout of a linear
- * layer), all three bf16, device memory, row-major and dense; fp32 accumulation, one rounding
- * to bf16 (nearest even) per output.  A plain GEMM, run by hipBLASLt.  The first call on a
- * device creates its hipBLASLt handle, and the first call on each (device, stream) a 32 MiB
- * workspace for that stream (all kept until the process ends), so calls on different streams
- * never share scratch memory; the first call for a (T, K, N) also picks the algorithm.  Host
- * calls serialise on a lock.  Errors: FG_E_ARG (null pointer, T < 0, K or N < 1), FG_E_UNSUPPORTED (no algorithm),
- * FG_E_HIP (a hipBLASLt or HIP error).  T = 0 does nothing. */
+ * layer), all three bf16, device memory, row-major, dense and 16-byte aligned; fp32
+ * accumulation, one rounding to bf16 (nearest even) per output.  This library's own bf16 MFMA
+ * GEMM for gfx950 (tile shape chosen from T and N); it allocates nothing and keeps no state.
+ * Errors: FG_E_ARG (null or unaligned pointer, T < 0, K or N < 1), FG_E_UNSUPPORTED (N not a
+ * multiple of 128 or K not a multiple of 64), FG_E_HIP.  T = 0 does nothing. */
 fg_status fg_linear_bf16(const void *x, const void *w, void *y, int32_t T, int32_t K, int32_t N,
                          void *stream);
 

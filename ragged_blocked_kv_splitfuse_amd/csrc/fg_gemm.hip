@@ -1,0 +1,236 @@
+// Dense projections either side of attention, as a gfx950 bf16 MFMA GEMM of this library.
+//
+// The QKV projection produces the rows fg_kv_append stores and fg_ragged_attention reads; the
+// output projection maps attention's rows back (DeepSpeed-FastGen paper card by Holmes et al.
+// 2024, "Key points": the kernels around attention come from FasterTransformer).  Both are
+//     y[T][N] = x[T][K] . w[N][K]^T        (w in the [out][in] layout of a linear layer)
+// with bf16 inputs, fp32 accumulation and one round-to-nearest-even to bf16 per output.
+//
+// Design (CDNA4): a workgroup of four waves (2 x 2) computes a (64*TT tokens) x (64*FT
+// features) tile; each wave owns FT x TT tiles of the 32x32x16 bf16 MFMA.  The MFMA computes the
+// transposed product C^T = W . X^T (A operand: 32 weight rows, B operand: 32 token rows; both
+// rows are contiguous along K, so every operand is one 16-byte load), which leaves each lane
+// with runs of four consecutive output features of one token: 8-byte stores of y rows.  The
+// inner dimension advances in BK-element stages; each stage's weight and token rows go from
+// memory straight into LDS with 16-byte LDS-DMA loads through an NSTG-deep ring, NSTG-1 stages
+// ahead of the math, swizzled so that the operand reads are free of bank conflicts.  The host
+// picks the tile by the number of workgroups it gives (ragged token counts run from a few rows
+// to thousands).  Tiles are placed per XCD where the shape allows (workgroup
+// b runs on XCD b % 8): each XCD takes a contiguous eighth of the output features, so its L2
+// holds that eighth of the weights while the token rows stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fg_internal.h"
+
+using fgi::fail;
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16;
+
+constexpr int GT = 256;    // threads: four waves, 2 x 2 over the tile
+constexpr int NUM_XCD = 8;
+
+template <int FT, int TT, int BK>
+struct Tile {
+  static constexpr int BN = 64 * FT;                 // output features per workgroup
+  static constexpr int BM = 64 * TT;                 // tokens per workgroup
+  static constexpr int ROW = BK * 2;                 // bytes per tile row of a stage
+  static constexpr int CH = BK / 8;                  // 16-byte chunks per row
+  static constexpr int STAGE = (BN + BM) * ROW;      // weight rows, then token rows
+  static constexpr int REGIONS = STAGE / 1024;       // 1 KiB per LDS-DMA wave instruction
+  static constexpr int W_REGIONS = BN * ROW / 1024;  // regions of weight rows
+  static constexpr int RPR = 1024 / ROW;             // rows per region
+  static constexpr int DPW = REGIONS / 4;            // LDS-DMA instructions per wave and stage
+  // ring depth: three stages where two workgroups per compute unit still fit in LDS
+  static constexpr int NSTG = 3 * STAGE <= 80 * 1024 ? 3 : 2;
+  static_assert(DPW * 4 == REGIONS && W_REGIONS * 1024 == BN * ROW, "regions");
+  static_assert(NSTG * STAGE <= 80 * 1024, "two workgroups per compute unit");
+};
+
+// 16-byte chunk c of tile row r sits at slot c ^ swz(r): the 16 lanes of one operand read (16
+// consecutive rows, one chunk) then hit 16 distinct 16-byte slots of a 256-byte window.  Rows
+// of 64 bytes (BK 32): four rows per window, the swizzle takes 4 values; rows of 128 bytes
+// (BK 64): two rows per window, 8 values.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7;
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// One wave instruction: 16 bytes per lane from global memory to LDS at lds + 16*lane (the LDS
+// base goes in M0, through the operand).  Untracked by the compiler; the kernel waits for these
+// with explicit vmcnt counts and orders them against LDS reads with barriers.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // s_waitcnt encoding (gfx9): vmcnt = bits 3:0 (+ bits 15:14), expcnt 6:4, lgkmcnt 11:8
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
+}
+
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int FT, int TT, int BK>
+__global__ __launch_bounds__(GT, 2) void gemm_nt_bf16_kernel(const u16 *__restrict__ x,
+                                                             const u16 *__restrict__ w,
+                                                             u16 *__restrict__ y, int T, int K,
+                                                             int N, int xcd_split) {
+  using Tl = Tile<FT, TT, BK>;
+  constexpr int BN = Tl::BN, BM = Tl::BM, ROW = Tl::ROW, DPW = Tl::DPW, NSTG = Tl::NSTG;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NSTG * Tl::STAGE];
+  const int NT = N / BN;
+  int mt, nt;
+  if (xcd_split) {  // XCD x takes column tiles [x * NT/8, (x+1) * NT/8), all row tiles
+    const int per = NT / NUM_XCD, b = blockIdx.x;
+    const int x8 = b % NUM_XCD, idx = b / NUM_XCD;
+    mt = idx / per;
+    nt = x8 * per + idx % per;
+  } else {
+    mt = blockIdx.x / NT;
+    nt = blockIdx.x % NT;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wf = wv >> 1, wt = wv & 1;  // this wave's features (wf) and tokens (wt)
+  const int f_base = nt * BN, t_base = mt * BM;
+
+  // LDS-DMA sources of this lane: wave wv fills regions p*4 + wv; a region is RPR tile rows
+  // (weight rows first, then token rows), lane -> (row, 16-byte slot)
+  const u16 *src[DPW];
+#pragma unroll
+  for (int p = 0; p < DPW; ++p) {
+    const int reg = p * 4 + wv;
+    const bool wrow = reg < Tl::W_REGIONS;
+    const int rr = Tl::RPR * (wrow ? reg : reg - Tl::W_REGIONS) + lane / Tl::CH;
+    const int c = (lane % Tl::CH) ^ swz<BK>(rr);
+    if (wrow)
+      src[p] = w + (size_t)(f_base + rr) * K + 8 * c;
+    else
+      src[p] = x + (size_t)min(t_base + rr, T - 1) * K + 8 * c;  // rows past T: read, unused
+  }
+  const uint32_t lds0 =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)ring;
+  auto issue = [&](int s) {  // stage s into buffer s % NSTG
+    const uint32_t base = lds0 + (uint32_t)(s % NSTG) * Tl::STAGE;
+#pragma unroll
+    for (int p = 0; p < DPW; ++p) dma16(src[p] + (size_t)s * BK, base + 1024u * (p * 4 + wv));
+  };
+
+  // operand rows of this lane: weights 32*FT*wf + 32*i + n, tokens 32*TT*wt + 32*j + n
+  int arow[FT], brow[TT];
+#pragma unroll
+  for (int i = 0; i < FT; ++i) arow[i] = 32 * FT * wf + 32 * i + n;
+#pragma unroll
+  for (int j = 0; j < TT; ++j) brow[j] = 32 * TT * wt + 32 * j + n;
+  f32x16 acc[FT][TT];
+#pragma unroll
+  for (int i = 0; i < FT; ++i)
+#pragma unroll
+    for (int j = 0; j < TT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nst = K / BK;
+#pragma unroll
+  for (int s = 0; s < NSTG - 1; ++s)
+    if (s < nst) issue(s);
+  for (int s = 0; s < nst; ++s) {
+    // this wave's loads of stage s landed (the later stages may still be in flight) ...
+    if (s + 1 < nst) wait_vm<DPW * (NSTG - 2)>();
+    else wait_vm<0>();
+    barrier();  // ... and every wave's; stage s-1 is consumed, its buffer free
+    if (s + NSTG - 1 < nst) issue(s + NSTG - 1);
+    const unsigned char *wb = ring + (s % NSTG) * Tl::STAGE;
+    const unsigned char *xb = wb + BN * ROW;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int c = 2 * ks + g;  // this lane's 8 inner elements: chunk c of its row
+      bf16x8 a[FT], b[TT];
+#pragma unroll
+      for (int i = 0; i < FT; ++i)
+        a[i] = *reinterpret_cast<const bf16x8 *>(wb + arow[i] * ROW + 16 * (c ^ swz<BK>(arow[i])));
+#pragma unroll
+      for (int j = 0; j < TT; ++j)
+        b[j] = *reinterpret_cast<const bf16x8 *>(xb + brow[j] * ROW + 16 * (c ^ swz<BK>(brow[j])));
+#pragma unroll
+      for (int i = 0; i < FT; ++i)
+#pragma unroll
+        for (int j = 0; j < TT; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    }
+  }
+
+  // epilogue: element e of acc[i][j] is feature 8*(e/4) + 4*g + e%4 of the i-th 32-feature
+  // block, for token n of the j-th 32-token block
+#pragma unroll
+  for (int j = 0; j < TT; ++j) {
+    const int t = t_base + 32 * TT * wt + 32 * j + n;
+    if (t >= T) continue;
+    u16 *yr = y + (size_t)t * N + f_base + 32 * FT * wf + 4 * g;
+#pragma unroll
+    for (int i = 0; i < FT; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[i][j][4 * q + e];
+        *reinterpret_cast<bf16x4 *>(yr + 32 * i + 8 * q) = v;
+      }
+  }
+}
+
+template <int FT, int TT, int BK>
+void launch(const u16 *x, const u16 *w, u16 *y, int T, int K, int N, hipStream_t st) {
+  using Tl = Tile<FT, TT, BK>;
+  const int NT = N / Tl::BN, MT = (T + Tl::BM - 1) / Tl::BM;
+  hipLaunchKernelGGL((gemm_nt_bf16_kernel<FT, TT, BK>), dim3((unsigned)(NT * MT)), dim3(GT), 0,
+                     st, x, w, y, T, K, N, NT % NUM_XCD == 0 ? 1 : 0);
+}
+
+}  // namespace
+
+extern "C" fg_status fg_linear_bf16(const void *x, const void *w, void *y, int32_t T, int32_t K,
+                                    int32_t N, void *stream) {
+  fgi::clear_error();
+  if (T < 0 || K < 1 || N < 1) return fail(FG_E_ARG, "sizes T=%d K=%d N=%d", T, K, N);
+  if (T == 0) return FG_OK;
+  if (!x || !w || !y) return fail(FG_E_ARG, "null x, w or y");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) |
+       reinterpret_cast<uintptr_t>(y)) & 15)
+    return fail(FG_E_ARG, "x, w and y must be 16-byte aligned");
+  if (N % 128 || K % 64)
+    return fail(FG_E_UNSUPPORTED, "the GEMM tiles need N %% 128 == 0 and K %% 64 == 0 (N=%d, K=%d)",
+                N, K);
+  if ((int64_t)T * (N / 128) > INT32_MAX) return fail(FG_E_UNSUPPORTED, "too many tiles");
+  const u16 *xp = (const u16 *)x, *wp = (const u16 *)w;
+  u16 *yp = (u16 *)y;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // the largest tile that still gives well over one workgroup per compute unit (the chip has
+  // 256), else the smallest.  Measured on the projection shapes (K 4096; N 4096 and 1024):
+  // 256 x 128 tiles pay from 512 workgroups on, 128 x 128 tiles from ~300.
+  const auto tiles = [&](int bm, int bn) { return (int64_t)((T + bm - 1) / bm) * (N / bn); };
+  constexpr int64_t WANT = 300;
+  if (N % 256 == 0 && tiles(128, 256) >= 512)
+    launch<4, 2, 32>(xp, wp, yp, T, K, N, st);
+  else if (tiles(128, 128) >= WANT)
+    launch<2, 2, 64>(xp, wp, yp, T, K, N, st);
+  else
+    launch<2, 1, 64>(xp, wp, yp, T, K, N, st);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_E_HIP, "GEMM launch: %s", hipGetErrorString(e));
+  return FG_OK;
+}
