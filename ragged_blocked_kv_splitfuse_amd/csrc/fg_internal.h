@@ -26,6 +26,7 @@ struct fg_cache {
   mutable std::vector<fgi::PlanItem> plan_base, plan_items;
   mutable std::vector<std::pair<float, int32_t>> plan_order;
   mutable std::vector<int32_t> plan_lists[8];  // per XCD record lists
+  mutable std::vector<int32_t> plan_se[8][4];  // per XCD and shader engine: record order
 };
 
 namespace fgi {

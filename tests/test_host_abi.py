@@ -367,14 +367,25 @@ def check_plan(hb, info, work, hq, hkv, head_dim=128):
     slot = {0: fg.FG_STREAM_ROWS * (head_dim + 2), 1: fg.FG_TILE_ROWS * (head_dim + 2)}
     groups = {}
     cover = {}
-    # the main list is laid out for the 8 XCDs (record i runs on XCD i % 8); lists that run
-    # short are padded with null records at their end
-    assert len(main) % 8 == 0
+    # the main list is laid out for the 8 XCDs (record i runs on XCD i % 8) and, within an
+    # XCD's sequence, for its 4 shader engines (position j on engine j % 4); each engine's
+    # list is padded with null records at its end only
+    assert len(main) % 32 == 0
+    for k in range(8):
+        for r in range(4):
+            sub = main[k::8][r::4]
+            null = [int(x[0]) == -1 for x in sub]
+            first = null.index(True) if True in null else len(null)
+            assert all(null[first:]), "padding only at a list's end"
+        # every engine of an XCD gets the same number of records of each kind, +-1
+        for mode in (0, 1):
+            n = [sum(1 for x in main[k::8][r::4] if int(x[0]) != -1 and int(x[6]) == mode)
+                 for r in range(4)]
+            assert max(n) - min(n) <= 1, ("records per shader engine", mode, n)
     xcd_of_tile_group = {}
     for i, rec in enumerate(main):
         if int(rec[0]) == -1:
             assert int(rec[7]) == -1
-            assert all(int(r[0]) == -1 for r in main[i::8]), "padding only at an XCD list's end"
             continue
         s, h, t0, nt, klo, khi, mode, grp, sp, nsp, poff = (int(x) for x in rec)
         if mode == 1 and hkv % 8 == 0:  # tile records of one (sequence, head) share an XCD
