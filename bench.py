@@ -168,8 +168,10 @@ def sweep_main(args):
 
 def time_pass(S, steps, warmup):
     """Warm up, then time `steps` identical passes (compose + plan + upload + kv_append +
-    attention) of the prepared workload.  Kernel times come from HIP events on the launch
-    stream; `elapsed` is the host clock over the timed steps, bracketed by synchronizations."""
+    attention) of the prepared workload.  `elapsed` is the host clock over the timed steps,
+    bracketed by synchronizations.  The attention time comes from HIP events around its launch
+    in the timed steps; the kv_append time from events around its launch in up to 20 further
+    steps after the timed region (the launch stream for both)."""
     import numpy as np
     import torch
     from ragged_blocked_kv_splitfuse_amd import fg
@@ -228,21 +230,33 @@ def time_pass(S, steps, warmup):
     attn_flops = 4 * w.head_dim * w.num_q_heads * pairs
     append_bytes = 4 * T * w.num_kv_heads * w.head_dim * e
 
+    # The timed steps carry two events each, around the attention launch (the roofline's
+    # kernel); the one after attention also guards the step's pinned descriptor buffer.  An
+    # event between the descriptor copy and kv_append would add a marker (and a few us of
+    # GPU idle time) to every step, so kv_append is timed in extra steps after the timed
+    # region instead, with events around it alone.
     n_total = warmup + steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(n_total)]
+    n_app = min(steps, 20)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_total + n_app)]
     host_s = []
 
-    def step(i):
+    def step(i, time_append=False):
         t0 = time.perf_counter()
         info, work = compose_and_plan()
-        c = desc.upload(hb, work, stream)
-        ev[i][0].record(stream)
+        c = desc.upload(hb, work, stream, record=False)
+        if time_append:
+            ev[i][0].record(stream)
         fg.fg_kv_append(h, c, k_new.data_ptr(), v_new.data_ptr(), sh)
-        ev[i][1].record(stream)
+        if time_append:
+            ev[i][1].record(stream)
+        else:
+            ev[i][0].record(stream)
         fg.fg_ragged_attention(h, c, info, desc.work_ptr, q.data_ptr(), w.num_q_heads, w.scale,
                                out.data_ptr(), wptr, wbytes, sh)
-        ev[i][2].record(stream)
+        if not time_append:
+            ev[i][1].record(stream)
+        desc.release(ev[i][1])
         restore_free_list()
         host_s.append(time.perf_counter() - t0)
         return info
@@ -255,15 +269,17 @@ def time_pass(S, steps, warmup):
         info = step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    for i in range(n_total, n_total + n_app):
+        step(i, time_append=True)
+    torch.cuda.synchronize()
     fg.fg_blocked_cache_destroy(h)
 
-    timed = ev[warmup:]
-    attn_ms = [a.elapsed_time(b2) for _, a, b2 in timed]   # attention launch only
-    app_ms = [a0.elapsed_time(a) for a0, a, _ in timed]
+    attn_ms = [a.elapsed_time(b) for a, b in ev[warmup:n_total]]   # attention launch only
+    app_ms = [a.elapsed_time(b) for a, b in ev[n_total:]]
     return dict(info=info, T=T, nseq=nseq, nq=nq, ctx=ctx, kv_tokens=kv_tokens,
                 attn_bytes=attn_bytes, attn_flops=attn_flops, append_bytes=append_bytes,
                 t_attn=float(np.mean(attn_ms)) * 1e-3, t_app=float(np.mean(app_ms)) * 1e-3,
-                elapsed=t1 - t0, q=q, k_new=k_new, v_new=v_new, host_s=host_s[warmup:])
+                elapsed=t1 - t0, q=q, k_new=k_new, v_new=v_new, host_s=host_s[warmup:n_total])
 
 
 def main():

@@ -100,7 +100,14 @@ class DeviceDescriptors:
             self.ring[i] = torch.empty(max(n, 1024), dtype=torch.int32, pin_memory=True)
         return i, self.ring[i]
 
-    def upload(self, hb: fg.HostBatch, work: np.ndarray | None = None, stream=None):
+    def upload(self, hb: fg.HostBatch, work: np.ndarray | None = None, stream=None,
+               record: bool = True):
+        """Copy the batch (and work list) to the device on `stream`.  The pinned staging
+        buffer is reused `ring` uploads later, once the event guarding it has completed:
+        with record=True an event recorded right after the copy; with record=False the caller
+        hands one in through release() (an event it records later on the same stream anyway,
+        e.g. after the pass's kernels), which saves a marker between the copy and the next
+        kernel."""
         S, stride = hb.num_seqs, hb.table_stride
         nw = 0 if work is None else int(work.size)
         parts = [hb.query_start[:S + 1], hb.n_query[:S], hb.context_len[:S],
@@ -120,9 +127,12 @@ class DeviceDescriptors:
         s = stream or torch.cuda.current_stream()
         with torch.cuda.stream(s):
             self.dev[:total].copy_(host[:total], non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(s)
+            ev = None
+            if record:
+                ev = torch.cuda.Event()
+                ev.record(s)
         self.events[i] = ev
+        self._last = i
         base = self.dev.data_ptr()
         offs = np.cumsum([0] + sizes)
         p32 = lambda k: ctypes.cast(base + 4 * int(offs[k]), fg.i32p)
@@ -133,6 +143,12 @@ class DeviceDescriptors:
         c.seq_id = None
         self.work_ptr = base + 4 * int(offs[4]) if nw else 0
         return c
+
+
+    def release(self, event):
+        """Guard the staging buffer of the last upload (made with record=False) by `event`,
+        recorded on the upload's stream after the copy."""
+        self.events[self._last] = event
 
 
 class Workspace:
