@@ -170,8 +170,8 @@ def time_pass(S, steps, warmup):
     """Warm up, then time `steps` identical passes (compose + plan + upload + kv_append +
     attention) of the prepared workload.  `elapsed` is the host clock over the timed steps,
     bracketed by synchronizations.  The attention time comes from HIP events around its launch
-    in the timed steps; the kv_append time from events around its launch in up to 20 further
-    steps after the timed region (the launch stream for both)."""
+    in every fourth timed step (and the last); the kv_append time from events around its launch
+    in up to 20 further steps after the timed region (the launch stream for both)."""
     import numpy as np
     import torch
     from ragged_blocked_kv_splitfuse_amd import fg
@@ -180,7 +180,7 @@ def time_pass(S, steps, warmup):
     w, cache, ss, hb = S["w"], S["cache"], S["ss"], S["hb"]
     arr_bytes, blocks0 = S["template"]
     free_ids = S["free_ids"]
-    desc = DeviceDescriptors(ring=4)
+    desc = DeviceDescriptors(ring=8)
     ws = Workspace()
     stream = torch.cuda.current_stream()
     sh = stream_handle(stream)
@@ -230,33 +230,38 @@ def time_pass(S, steps, warmup):
     attn_flops = 4 * w.head_dim * w.num_q_heads * pairs
     append_bytes = 4 * T * w.num_kv_heads * w.head_dim * e
 
-    # The timed steps carry two events each, around the attention launch (the roofline's
-    # kernel); the one after attention also guards the step's pinned descriptor buffer.  An
-    # event between the descriptor copy and kv_append would add a marker (and a few us of
-    # GPU idle time) to every step, so kv_append is timed in extra steps after the timed
-    # region instead, with events around it alone.
+    # Every fourth timed step carries two events around the attention launch (the roofline's
+    # kernel; the one after attention also guards the pinned descriptor buffers of the steps
+    # since the last guard).  Each event recorded on the stream adds a marker and several us of
+    # GPU idle time to its step, so the other steps carry none, and kv_append is timed in extra
+    # steps after the timed region, with events around it alone.
     n_total = warmup + steps
     n_app = min(steps, 20)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_total + n_app)]
+    timed_attn = []
     host_s = []
 
     def step(i, time_append=False):
         t0 = time.perf_counter()
         info, work = compose_and_plan()
         c = desc.upload(hb, work, stream, record=False)
+        mark = not time_append and (i % 4 == 3 or i == n_total - 1)
         if time_append:
             ev[i][0].record(stream)
         fg.fg_kv_append(h, c, k_new.data_ptr(), v_new.data_ptr(), sh)
         if time_append:
             ev[i][1].record(stream)
-        else:
+        if mark:
             ev[i][0].record(stream)
         fg.fg_ragged_attention(h, c, info, desc.work_ptr, q.data_ptr(), w.num_q_heads, w.scale,
                                out.data_ptr(), wptr, wbytes, sh)
-        if not time_append:
+        if mark:
             ev[i][1].record(stream)
-        desc.release(ev[i][1])
+            if i >= warmup:
+                timed_attn.append(i)
+        if mark or time_append:
+            desc.release(ev[i][1])
         restore_free_list()
         host_s.append(time.perf_counter() - t0)
         return info
@@ -274,7 +279,7 @@ def time_pass(S, steps, warmup):
     torch.cuda.synchronize()
     fg.fg_blocked_cache_destroy(h)
 
-    attn_ms = [a.elapsed_time(b) for a, b in ev[warmup:n_total]]   # attention launch only
+    attn_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed_attn]   # attention launch only
     app_ms = [a.elapsed_time(b) for a, b in ev[n_total:]]
     return dict(info=info, T=T, nseq=nseq, nq=nq, ctx=ctx, kv_tokens=kv_tokens,
                 attn_bytes=attn_bytes, attn_flops=attn_flops, append_bytes=append_bytes,

@@ -90,10 +90,14 @@ class DeviceDescriptors:
         self.dev = None
         self.cstruct = fg.FgRaggedBatch()
         self.work_ptr = 0
+        self._pending = []  # slots uploaded with record=False and not yet released
 
     def _staging(self, n):
         i = self.slot
         self.slot = (self.slot + 1) % len(self.ring)
+        if i in self._pending:
+            raise RuntimeError("descriptor ring reused before release(): call release() at "
+                               "least once every ring uploads")
         if self.events[i] is not None:
             self.events[i].synchronize()        # the copy that last read this buffer is done
         if self.ring[i] is None or self.ring[i].numel() < n:
@@ -132,7 +136,10 @@ class DeviceDescriptors:
                 ev = torch.cuda.Event()
                 ev.record(s)
         self.events[i] = ev
-        self._last = i
+        if record:
+            self._pending = []
+        else:
+            self._pending.append(i)
         base = self.dev.data_ptr()
         offs = np.cumsum([0] + sizes)
         p32 = lambda k: ctypes.cast(base + 4 * int(offs[k]), fg.i32p)
@@ -146,9 +153,12 @@ class DeviceDescriptors:
 
 
     def release(self, event):
-        """Guard the staging buffer of the last upload (made with record=False) by `event`,
-        recorded on the upload's stream after the copy."""
-        self.events[self._last] = event
+        """Guard the staging buffers of the uploads made with record=False since the last
+        release by `event`, recorded on the upload stream after their copies.  Call it at least
+        once every `ring` uploads: a buffer is reused only after its guard completed."""
+        for i in self._pending:
+            self.events[i] = event
+        self._pending = []
 
 
 class Workspace:
