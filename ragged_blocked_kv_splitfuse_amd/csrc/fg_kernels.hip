@@ -1076,7 +1076,7 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(
 // small pass (a few hundred decode tokens, or a 512-token chunk) still spreads over the chip.
 // ---------------------------------------------------------------------------------------
 constexpr int APPEND_THREADS = 256;
-constexpr int64_t APPEND_MIN_WGS = 1024;  // four per compute unit
+constexpr int64_t APPEND_MIN_WGS = 2048;  // eight per compute unit
 
 template <typename T, int HD, int TOK>
 __global__ __launch_bounds__(APPEND_THREADS) void kv_append_kernel(
