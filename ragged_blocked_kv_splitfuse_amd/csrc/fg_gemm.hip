@@ -7,7 +7,8 @@
 // with bf16 inputs, fp32 accumulation and one round-to-nearest-even to bf16 per output.
 //
 // Design (CDNA4): a workgroup of four waves (2 x 2) computes a (64*TT tokens) x (64*FT
-// features) tile; each wave owns FT x TT tiles of the 32x32x16 bf16 MFMA.  The MFMA computes the
+// features) tile; each wave owns FT x TT tiles of the 32x32x16 bf16 MFMA (up to 4 x 4, whose
+// 256 accumulators per lane live in AGPRs, one wave per SIMD).  The MFMA computes the
 // transposed product C^T = W . X^T (A operand: 32 weight rows, B operand: 32 token rows; both
 // rows are contiguous along K, so every operand is one 16-byte load), which leaves each lane
 // with runs of four consecutive output features of one token: 8-byte stores of y rows.  The
@@ -47,10 +48,14 @@ struct Tile {
   static constexpr int W_REGIONS = BN * ROW / 1024;  // regions of weight rows
   static constexpr int RPR = 1024 / ROW;             // rows per region
   static constexpr int DPW = REGIONS / 4;            // LDS-DMA instructions per wave and stage
-  // ring depth: three stages where two workgroups per compute unit still fit in LDS
-  static constexpr int NSTG = 3 * STAGE <= 80 * 1024 ? 3 : 2;
+  // Workgroups per compute unit: 4 x 4 MFMA tiles per wave keep 256 accumulators per lane (in
+  // AGPRs), which leaves room for one wave per SIMD; smaller tiles run two workgroups per CU.
+  static constexpr int WGS = FT * TT >= 16 ? 1 : 2;
+  // ring depth: three stages where the workgroups of a compute unit still fit in LDS
+  static constexpr int LDS_PER_WG = (WGS == 1 ? 144 : 80) * 1024;
+  static constexpr int NSTG = 3 * STAGE <= LDS_PER_WG ? 3 : 2;
   static_assert(DPW * 4 == REGIONS && W_REGIONS * 1024 == BN * ROW, "regions");
-  static_assert(NSTG * STAGE <= 80 * 1024, "two workgroups per compute unit");
+  static_assert(NSTG * STAGE <= LDS_PER_WG, "the ring must fit the workgroups of a CU");
 };
 
 // 16-byte chunk c of tile row r sits at slot c ^ swz(r): the 16 lanes of one operand read (16
@@ -86,7 +91,7 @@ __device__ __forceinline__ void barrier() {
 }
 
 template <int FT, int TT, int BK>
-__global__ __launch_bounds__(GT, 2) void gemm_nt_bf16_kernel(const u16 *__restrict__ x,
+__global__ __launch_bounds__(GT, FT * TT >= 16 ? 1 : 2) void gemm_nt_bf16_kernel(const u16 *__restrict__ x,
                                                              const u16 *__restrict__ w,
                                                              u16 *__restrict__ y, int T, int K,
                                                              int N, int xcd_split) {
@@ -219,12 +224,19 @@ extern "C" fg_status fg_linear_bf16(const void *x, const void *w, void *y, int32
   const u16 *xp = (const u16 *)x, *wp = (const u16 *)w;
   u16 *yp = (u16 *)y;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // the largest tile that still gives well over one workgroup per compute unit (the chip has
-  // 256), else the smallest.  Measured on the projection shapes (K 4096; N 4096 and 1024):
-  // 256 x 128 tiles pay from 512 workgroups on, 128 x 128 tiles from ~300.
+  // 256 x 256 tiles (one workgroup per compute unit, the chip has 256) when every round of
+  // workgroups, the last one included, fills at least ~200 of the CUs; else the largest other
+  // tile that still gives well over one workgroup per compute unit, else the smallest.
+  // Measured on the projection shapes (K 4096; N 12288, 6144 and 4096; T 512 to 4096):
+  // 256 x 256 tiles gain 10-20% at 240 and 768 workgroups, lose ~10-14% at 384 (a half-empty
+  // last round) and ~25-60% below 200 workgroups; 256 x 128 tiles pay from 512 workgroups on,
+  // 128 x 128 tiles from ~300.
   const auto tiles = [&](int bm, int bn) { return (int64_t)((T + bm - 1) / bm) * (N / bn); };
-  constexpr int64_t WANT = 300;
-  if (N % 256 == 0 && tiles(128, 256) >= 512)
+  constexpr int64_t WANT = 300, CUS = 256, FULL = 200;
+  const int64_t t44 = N % 256 == 0 ? tiles(256, 256) : 0, rem = t44 % CUS;
+  if (t44 >= FULL && (rem == 0 || rem >= FULL))
+    launch<4, 4, 32>(xp, wp, yp, T, K, N, st);
+  else if (N % 256 == 0 && tiles(128, 256) >= 512)
     launch<4, 2, 32>(xp, wp, yp, T, K, N, st);
   else if (tiles(128, 128) >= WANT)
     launch<2, 2, 64>(xp, wp, yp, T, K, N, st);
