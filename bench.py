@@ -291,8 +291,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
-              "multi-GPU path; the pass shards by KV head or by sequence with no exchange "
-              "inside it, see the design notes.", file=sys.stderr)
+              "multi-GPU path; the pass would shard by KV head or by sequence, with no "
+              "exchange inside it.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

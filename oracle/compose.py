@@ -11,7 +11,7 @@ Policy (DeepSpeed-FastGen paper card by Holmes et al. 2024, "Summary" and
   the budget is filled exactly whenever demand allows;
 * if demand is below B the pass is simply shorter (no padding).
 
-Readings where the pages are silent (each one is listed in the design notes):
+Readings where the pages are silent:
 
 * phase: a sequence is in its prompt phase while ``n_cached < prompt_len``,
   otherwise it decodes one token;

@@ -7,7 +7,7 @@ runs at the fixed token budget; long prompts are chunked over passes, short prom
 generation tokens fill it); blog "1. Introduction" (each request is prompt processing, then
 generation, one token per step).
 
-Readings where the pages are silent (each one is listed in the design notes):
+Readings where the pages are silent:
 
 * a request with P prompt tokens and O generated tokens: the pass that takes its last prompt
   token yields the first generated token; every later pass feeds one generated token back
