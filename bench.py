@@ -340,7 +340,7 @@ def main():
                    "split_groups": int(info.num_groups)},
         "roofline": roof,
         "per_config": per_config,
-        "hbm_reference": hbm_reference() if args.per_config else None,
+        "hbm_reference": hbm_reference(append_bytes=append_bytes) if args.per_config else None,
         "kernels": {"attention_us": t_attn * 1e6, "kv_append_us": t_app * 1e6,
                     "kv_append_GBps": append_bytes / t_app / 1e9,
                     "gpu_only_tokens_per_s": T / (t_attn + t_app),
@@ -511,10 +511,14 @@ def config_entry(w, r, bound):
             "split_groups": int(r["info"].num_groups), "work_records": int(r["info"].num_work)}
 
 
-def hbm_reference(gib=4, reps=10):
+def hbm_reference(gib=4, reps=10, append_bytes=0):
     """Practical HBM rates on this device, measured beside the pass: a device-to-device copy
     of `gib` GiB (bytes read + written per second) and a read-only reduction of 2*`gib` GiB
-    (torch's own kernels), both timed with events over `reps` repetitions."""
+    (torch's own kernels), both timed with events over `reps` repetitions.  With append_bytes,
+    also a plain copy moving that many bytes (half read, half written, as kv_append does) with
+    1 GiB of other copy traffic before each repetition, so that it starts from cold caches as
+    kv_append does after an attention pass: the median event-timed duration of 20."""
+    import numpy as np
     import torch
     n = gib << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -532,10 +536,30 @@ def hbm_reference(gib=4, reps=10):
         e1.record()
         torch.cuda.synchronize()
         out[name + "_GBps"] = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del a, b, x
+    del x
+    if append_bytes:
+        n2 = append_bytes // 2
+        src = torch.empty(n2, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        flush_src, flush_dst = a[: 1 << 29], b[: 1 << 29]
+        ts = []
+        for _ in range(20):
+            flush_dst.copy_(flush_src)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dst.copy_(src)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        out["append_size_cold_copy_us"] = float(np.median(ts))
+        out["append_size_bytes"] = int(2 * n2)
+        del src, dst, flush_src, flush_dst
+    del a, b
     torch.cuda.empty_cache()
     out["how"] = (f"torch device copy of {gib} GiB (read + write bytes) and torch sum over "
-                  f"{2 * gib} GiB of fp32 (read bytes), {reps} repetitions each")
+                  f"{2 * gib} GiB of fp32 (read bytes), {reps} repetitions each" +
+                  ("; a copy moving kv_append's bytes after 1 GiB of other traffic, median of 20"
+                   if append_bytes else ""))
     return out
 
 
