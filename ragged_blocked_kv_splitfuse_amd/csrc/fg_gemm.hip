@@ -13,8 +13,10 @@
 // rows are contiguous along K, so every operand is one 16-byte load), which leaves each lane
 // with runs of four consecutive output features of one token: 8-byte stores of y rows.  The
 // inner dimension advances in BK-element stages; each stage's weight and token rows go from
-// memory straight into LDS with 16-byte LDS-DMA loads through an NSTG-deep ring, NSTG-1 stages
-// ahead of the math, swizzled so that the operand reads are free of bank conflicts.  The host
+// memory straight into LDS with 16-byte LDS-DMA loads through an NSTG-deep ring, each buffer
+// refilled as soon as every wave has read it, swizzled so that the operand reads are free of
+// bank conflicts.  The operand reads run one MFMA k-step ahead of the products (two register
+// sets), interleaved with them, so the matrix cores do not wait for LDS.  The host
 // picks the tile by the number of workgroups it gives (ragged token counts run from a few rows
 // to thousands).  Tiles are placed per XCD where the shape allows (workgroup
 // b runs on XCD b % 8): each XCD takes a contiguous eighth of the output features, so its L2
@@ -51,7 +53,7 @@ struct Tile {
   // Workgroups per compute unit: 4 x 4 MFMA tiles per wave keep 256 accumulators per lane (in
   // AGPRs), which leaves room for one wave per SIMD; smaller tiles run two workgroups per CU.
   static constexpr int WGS = FT * TT >= 16 ? 1 : 2;
-  // ring depth: three stages where the workgroups of a compute unit still fit in LDS
+  // ring depth: three stages where the workgroups of a compute unit still fit in LDS, else two
   static constexpr int LDS_PER_WG = (WGS == 1 ? 144 : 80) * 1024;
   static constexpr int NSTG = 3 * STAGE <= LDS_PER_WG ? 3 : 2;
   static_assert(DPW * 4 == REGIONS && W_REGIONS * 1024 == BN * ROW, "regions");
@@ -151,31 +153,71 @@ __global__ __launch_bounds__(GT, FT * TT >= 16 ? 1 : 2) void gemm_nt_bf16_kernel
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nst = K / BK;
-#pragma unroll
-  for (int s = 0; s < NSTG - 1; ++s)
-    if (s < nst) issue(s);
-  for (int s = 0; s < nst; ++s) {
-    // this wave's loads of stage s landed (the later stages may still be in flight) ...
-    if (s + 1 < nst) wait_vm<DPW * (NSTG - 2)>();
+  constexpr int KS = BK / 16;  // MFMA k-steps per stage (even)
+  static_assert(KS % 2 == 0, "operand double buffer alternates within a stage");
+  // wait until at most n stages of this wave's LDS-DMA loads are in flight (n in 0 .. 3)
+  auto wait_stages = [&](int n) {
+    if (n >= 3) wait_vm<3 * DPW>();
+    else if (n == 2) wait_vm<2 * DPW>();
+    else if (n == 1) wait_vm<DPW>();
     else wait_vm<0>();
-    barrier();  // ... and every wave's; stage s-1 is consumed, its buffer free
-    if (s + NSTG - 1 < nst) issue(s + NSTG - 1);
+  };
+  // operands of k-step ks of stage s into register set r
+  bf16x8 a[2][FT], b[2][TT];
+  auto read_ops = [&](int s, int ks, int r) {
     const unsigned char *wb = ring + (s % NSTG) * Tl::STAGE;
     const unsigned char *xb = wb + BN * ROW;
+    const int c = 2 * ks + g;  // this lane's 8 inner elements: chunk c of its row
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = 2 * ks + g;  // this lane's 8 inner elements: chunk c of its row
-      bf16x8 a[FT], b[TT];
+    for (int i = 0; i < FT; ++i)
+      a[r][i] = *reinterpret_cast<const bf16x8 *>(wb + arow[i] * ROW + 16 * (c ^ swz<BK>(arow[i])));
 #pragma unroll
-      for (int i = 0; i < FT; ++i)
-        a[i] = *reinterpret_cast<const bf16x8 *>(wb + arow[i] * ROW + 16 * (c ^ swz<BK>(arow[i])));
+    for (int j = 0; j < TT; ++j)
+      b[r][j] = *reinterpret_cast<const bf16x8 *>(xb + brow[j] * ROW + 16 * (c ^ swz<BK>(brow[j])));
+  };
+  // the products of one k-step, with the next k-step's operand reads (issued just before)
+  // placed between its first products, one after each, so that they land well before the
+  // next k-step needs them
+  auto products = [&](int r) {
 #pragma unroll
-      for (int j = 0; j < TT; ++j)
-        b[j] = *reinterpret_cast<const bf16x8 *>(xb + brow[j] * ROW + 16 * (c ^ swz<BK>(brow[j])));
+    for (int i = 0; i < FT; ++i)
 #pragma unroll
-      for (int i = 0; i < FT; ++i)
+      for (int j = 0; j < TT; ++j) acc[i][j] = mfma32(a[r][i], b[r][j], acc[i][j]);
 #pragma unroll
-        for (int j = 0; j < TT; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    for (int q = 0; q < FT + TT; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+  };
+
+  // Every buffer of the ring is filled ahead; stage s's buffer is refilled (stage s + NSTG)
+  // once every wave has read all of stage s, i.e. after the barrier that also makes stage
+  // s + 1 visible.  The operand reads run one k-step ahead of the products, across that
+  // barrier too, so the matrix cores do not wait for LDS between k-steps.
+#pragma unroll
+  for (int s = 0; s < NSTG; ++s)
+    if (s < nst) issue(s);
+  wait_stages(min(nst - 1, NSTG - 1));
+  barrier();
+  read_ops(0, 0, 0);
+  for (int s = 0; s < nst; ++s) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) {
+        read_ops(s, ks + 1, cur ^ 1);
+      } else {
+        // stage s fully read by this wave (its last operands are in registers), stage s + 1
+        // landed for this wave; the barrier extends both to every wave.  After the last stage
+        // this reads a stale buffer into registers that are never used, so that no branch
+        // leaves the compiler unsure which LDS reads are still in flight.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        wait_stages(max(0, min(nst - 2 - s, NSTG - 2)));
+        barrier();
+        if (s + NSTG < nst) issue(s + NSTG);
+        read_ops(s + 1, 0, cur ^ 1);
+      }
+      products(cur);
     }
   }
 
@@ -206,6 +248,129 @@ void launch(const u16 *x, const u16 *w, u16 *y, int T, int K, int N, hipStream_t
                      st, x, w, y, T, K, N, NT % NUM_XCD == 0 ? 1 : 0);
 }
 
+// ---------------------------------------------------------------------------------------
+// Few token rows (T <= 64, the passes of a serving loop that carry only decode tokens): the
+// product is a stream of the weights, read once, against a handful of token rows that every
+// workgroup reads from L2.  One workgroup of eight waves per 16 output features (N / 16
+// workgroups: 256 for N = 4096).  The inner dimension advances in SKK-element stages; a stage
+// holds the 16 weight rows and the 16 * NT token rows (rows past T repeat row T-1, unused) and
+// goes to LDS by LDS-DMA in whole rows, three stages deep: loaded straight into MFMA operand
+// registers, each instruction would read half of 16 cache lines, at about a third of the rate
+// of whole lines.  Wave w takes the k-steps w, w + 8, ... of every stage (16x16x32 bf16 MFMA,
+// C^T = W . X^T); the eight partial tiles are summed through LDS in wave order (deterministic),
+// rounded once to bf16 and stored.
+// ---------------------------------------------------------------------------------------
+constexpr int SK_THREADS = 512;  // eight waves
+constexpr int SK_WAVES = SK_THREADS / 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int NT>
+struct Skinny {
+  static constexpr int SKK = NT <= 2 ? 512 : 256;  // inner elements per stage
+  static constexpr int ROWS = 16 + 16 * NT;         // weight rows, then token rows
+  static constexpr int ROWB = SKK * 2;              // bytes per stage row
+  static constexpr int STAGE = ROWS * ROWB;
+  static constexpr int NI = STAGE / 1024;           // LDS-DMA instructions per stage
+  static constexpr int DPW = NI / SK_WAVES;         // ... per wave
+  static constexpr int RPI = 1024 / ROWB;           // rows per instruction
+  static constexpr int KSW = SKK / 32 / SK_WAVES;   // k-steps per wave and stage
+  static constexpr int NSTG = 3;
+  static_assert(DPW * SK_WAVES == NI && KSW >= 1, "stage split");
+  static_assert(NSTG * STAGE <= 144 * 1024, "ring");
+};
+
+// 16-byte chunk c of stage row r sits at slot c ^ (r & 15): 16 lanes reading one chunk of 16
+// consecutive rows hit 16 distinct slots of a 256-byte window.
+template <int NT>
+__global__ __launch_bounds__(SK_THREADS) void gemm_skinny_bf16_kernel(const u16 *__restrict__ x,
+                                                                       const u16 *__restrict__ w,
+                                                                       u16 *__restrict__ y, int T,
+                                                                       int K, int N) {
+  using Sk = Skinny<NT>;
+  constexpr int ROWB = Sk::ROWB, DPW = Sk::DPW, NSTG = Sk::NSTG;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NSTG * Sk::STAGE];
+  const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int f0 = blockIdx.x * 16;
+  // LDS-DMA sources of this lane: instruction p*8 + wv fills stage rows RPI*(p*8+wv) ..
+  const u16 *src[DPW];
+#pragma unroll
+  for (int p = 0; p < DPW; ++p) {
+    const int ins = p * SK_WAVES + wv;
+    const int row = Sk::RPI * ins + lane / (ROWB / 16);
+    const int c = (lane % (ROWB / 16)) ^ (row & 15);
+    src[p] = row < 16 ? w + (size_t)(f0 + row) * K + 8 * c
+                      : x + (size_t)min(row - 16, T - 1) * K + 8 * c;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)ring;
+  auto issue = [&](int s) {
+    const uint32_t base = lds0 + (uint32_t)(s % NSTG) * Sk::STAGE;
+#pragma unroll
+    for (int p = 0; p < DPW; ++p)
+      dma16(src[p] + (size_t)s * Sk::SKK, base + 1024u * (p * SK_WAVES + wv));
+  };
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nst = K / Sk::SKK;
+#pragma unroll
+  for (int s = 0; s < NSTG - 1; ++s)
+    if (s < nst) issue(s);
+  for (int s = 0; s < nst; ++s) {
+    // this wave's loads of stage s landed (the next stage may still be in flight) ...
+    if (s + 1 < nst) wait_vm<DPW>();
+    else wait_vm<0>();
+    barrier();  // ... and every wave's; stage s-1 is consumed, its buffer free
+    if (s + NSTG - 1 < nst) issue(s + NSTG - 1);
+    const unsigned char *sb = ring + (s % NSTG) * Sk::STAGE;
+#pragma unroll
+    for (int q = 0; q < Sk::KSW; ++q) {
+      const int c = 4 * (q * SK_WAVES + wv) + g;  // chunk of this lane's 8 inner elements
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sb + r * ROWB + 16 * (c ^ r));
+      bf16x8 b[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int row = 16 + 16 * j + r;
+        b[j] = *reinterpret_cast<const bf16x8 *>(sb + row * ROWB + 16 * (c ^ (row & 15)));
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = mfma16(a, b[j], acc[j]);
+    }
+  }
+  barrier();  // every wave is done with the ring
+  // element e of acc[j] (lane l): feature 4*(l/16) + e, token 16*j + l%16
+  float *part = reinterpret_cast<float *>(ring);  // [wave][NT][64 lanes][4]
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+    *reinterpret_cast<f32x4 *>(part + ((wv * NT + j) * 64 + lane) * 4) = acc[j];
+  __syncthreads();
+  for (int q = threadIdx.x; q < NT * 64; q += SK_THREADS) {  // (tile, lane) pairs
+    const int j = q >> 6, l = q & 63;
+    const int t = 16 * j + (l & 15);
+    f32x4 sum = *reinterpret_cast<const f32x4 *>(part + (j * 64 + l) * 4);
+#pragma unroll
+    for (int u = 1; u < SK_WAVES; ++u)
+      sum += *reinterpret_cast<const f32x4 *>(part + ((u * NT + j) * 64 + l) * 4);
+    if (t < T) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)sum[e];
+      *reinterpret_cast<bf16x4 *>(y + (size_t)t * N + f0 + 4 * (l >> 4)) = v;
+    }
+  }
+}
+
+template <int NT>
+void launch_skinny(const u16 *x, const u16 *w, u16 *y, int T, int K, int N, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_skinny_bf16_kernel<NT>), dim3((unsigned)(N / 16)), dim3(SK_THREADS),
+                     0, st, x, w, y, T, K, N);
+}
+
 }  // namespace
 
 extern "C" fg_status fg_linear_bf16(const void *x, const void *w, void *y, int32_t T, int32_t K,
@@ -224,18 +389,30 @@ extern "C" fg_status fg_linear_bf16(const void *x, const void *w, void *y, int32
   const u16 *xp = (const u16 *)x, *wp = (const u16 *)w;
   u16 *yp = (u16 *)y;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // 256 x 256 tiles (one workgroup per compute unit, the chip has 256) when every round of
-  // workgroups, the last one included, fills at least ~200 of the CUs; else the largest other
-  // tile that still gives well over one workgroup per compute unit, else the smallest.
+  // 256 x 256 tiles (64-wide stages, one workgroup per compute unit, the chip has 256) when
+  // every round of workgroups, the last one included, fills at least ~200 of the CUs; else the
+  // largest other tile that still gives well over one workgroup per compute unit, else the
+  // smallest.
   // Measured on the projection shapes (K 4096; N 12288, 6144 and 4096; T 512 to 4096):
   // 256 x 256 tiles gain 10-20% at 240 and 768 workgroups, lose ~10-14% at 384 (a half-empty
   // last round) and ~25-60% below 200 workgroups; 256 x 128 tiles pay from 512 workgroups on,
   // 128 x 128 tiles from ~300.
+  // Up to 64 token rows: the weight-streaming kernel (whole stages of 512 or 256 inner
+  // elements).
+  if (T <= 64 && K % 512 == 0) {
+    if (T <= 16) launch_skinny<1>(xp, wp, yp, T, K, N, st);
+    else if (T <= 32) launch_skinny<2>(xp, wp, yp, T, K, N, st);
+    else if (T <= 48) launch_skinny<3>(xp, wp, yp, T, K, N, st);
+    else launch_skinny<4>(xp, wp, yp, T, K, N, st);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(FG_E_HIP, "GEMM launch: %s", hipGetErrorString(e));
+    return FG_OK;
+  }
   const auto tiles = [&](int bm, int bn) { return (int64_t)((T + bm - 1) / bm) * (N / bn); };
   constexpr int64_t WANT = 300, CUS = 256, FULL = 200;
   const int64_t t44 = N % 256 == 0 ? tiles(256, 256) : 0, rem = t44 % CUS;
   if (t44 >= FULL && (rem == 0 || rem >= FULL))
-    launch<4, 4, 32>(xp, wp, yp, T, K, N, st);
+    launch<4, 4, 64>(xp, wp, yp, T, K, N, st);
   else if (N % 256 == 0 && tiles(128, 256) >= 512)
     launch<4, 2, 32>(xp, wp, yp, T, K, N, st);
   else if (tiles(128, 128) >= WANT)
