@@ -67,6 +67,13 @@ __device__ __forceinline__ uint4 ld16(const void *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }
 
+// the same with the non-temporal hint (data read once: L2 lines it fills are the first evicted)
+__device__ __forceinline__ uint4 ld16_nt(const void *p) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v t = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
 // eight fp32 values -> eight bf16 (hardware round-to-nearest-even conversion)
 __device__ __forceinline__ bf16x8 to_bf16x8(const float *p) {
   bf16x8 r;
@@ -140,11 +147,6 @@ typedef __attribute__((address_space(4))) const int32_t cint32_t;
 __device__ __forceinline__ int ldc(const int32_t *p, size_t i) {
   return ((cint32_t *)p)[i];
 }
-
-// Swizzles of the LDS tiles (16-byte chunk index XOR a row function) that make the MFMA
-// operand reads and the cooperative tile writes free of bank conflicts.
-__device__ __forceinline__ int swz_k(int key) { return ((key >> 1) & 12) | (key & 3); }
-__device__ __forceinline__ int swz_v(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
 struct Params {
   const int32_t *items;  // work items, FG_ITEM_INTS each
@@ -304,10 +306,93 @@ __device__ void merge_splits(const Params &P, const Rec &R) {
   }
 }
 
+// One wave instruction: 16 bytes per lane from global memory to LDS at lds_wave_base + 16*lane.
+// Written as inline asm so that the compiler does not track these loads: its alias tracking of
+// LDS-DMA targets is easily lost and then drains every prefetched stage before ordinary LDS
+// reads.  The LDS base goes in through an "{m0}" operand, so the compiler itself writes M0 and
+// knows it is in use.  The kernel waits for the loads itself (wait_dma) and separates them from
+// LDS reads by barriers; the "memory" clobber keeps the compiler from moving memory operations
+// across them.
+__device__ __forceinline__ void dma16(const u16 *src, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "{m0}"(lds_addr)
+               : "memory");
+}
+
+// the same with the non-temporal hint, for data read once
+__device__ __forceinline__ void dma16_nt(const u16 *src, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(src), "{m0}"(lds_addr)
+               : "memory");
+}
+
+// LDS byte address of a workgroup-shared array (a constant once the array is known)
+__device__ __forceinline__ uint32_t lds_addr_of(const u16 *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const u16 *)p;
+}
+
+// Workgroup barrier for the stage ring.  __syncthreads() would also drain every vector load
+// still in flight (its fence waits for all of them), i.e. the prefetched stages; here the
+// data a stage needs is already covered by wait_dma, and LDS reads complete before their
+// MFMAs consume them, so a bare barrier suffices.  The empty asm statements keep the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// wait until at most n of this wave's LDS-DMA loads are outstanding (n in 0 .. 16)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // s_waitcnt encoding (gfx9): vmcnt = bits 3:0 (+ bits 15:14), expcnt 6:4, lgkmcnt 11:8
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
+}
+__device__ __forceinline__ void wait_dma(int n) {
+  switch (n) {
+    case 0: wait_vm<0>(); break;   case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;   case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;   case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;   case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;   case 9: wait_vm<9>(); break;
+    case 10: wait_vm<10>(); break; case 11: wait_vm<11>(); break;
+    case 12: wait_vm<12>(); break; case 13: wait_vm<13>(); break;
+    case 14: wait_vm<14>(); break; case 15: wait_vm<15>(); break;
+    default: wait_vm<16>(); break;
+  }
+}
+
+// Stream records stage each 64-key tile's K rows in the wave's own LDS region.  Loaded straight
+// into MFMA operand registers, one instruction reads the same 64-byte quarter of 16 key rows, i.e.
+// half of 16 cache lines; a CU then moves about a third of what it moves for whole lines (probe:
+// 37 against 116 GB/s per CU with the chip otherwise idle).  The LDS-DMA instead fetches whole
+// rows (RPI rows of 2*HD bytes per instruction), and the operand reads come from LDS.  With
+// every request a whole line, the stream's K and V loads carry the non-temporal hint: a decode
+// row's history is read once, and its lines no longer push the chunk rows' K/V out of L2 (with
+// half-line requests the hint made the second half miss).  Chunk c of
+// key row `key` sits at slot c ^ swz_s<HD>(key): the 16 rows of one operand read (key bits 0, 1,
+// 3, 4 vary; bit 2 and 5 are fixed) then fall on 16 distinct 16-byte slots of the bank window (at
+// HD 64 two rows share a window: the row's parity picks the half, the swizzle takes 8 values).
+template <int HD>
+struct StreamK {
+  static constexpr int CPR = HD / 8;         // 16-byte chunks per key row
+  static constexpr int RPI = 64 / CPR;       // key rows per DMA instruction (1 KiB)
+  static constexpr int NDMA = KEY_TILE / RPI;  // DMA instructions per tile
+  static constexpr int ELEMS = KEY_TILE * HD;  // u16 elements of a wave's region
+};
+template <int HD>
+__device__ __forceinline__ int swz_s(int key) {
+  if (HD == 128) return ((key >> 1) & 12) | (key & 3);
+  return ((key >> 1) & 1) | ((key >> 2) & 6);
+}
+
 // ---------------------------------------------------------------------------------------
-// MODE_STREAM: <= 16 query rows.  Each wave streams its own key tiles (w, w + NW, ...)
-// straight from HBM into MFMA operand registers (no LDS staging, no barriers), then the NW
-// waves merge their running states through LDS.
+// MODE_STREAM: <= 16 query rows.  Each wave streams its own key tiles (w, w + NW, ...) from
+// HBM: V straight into MFMA operand registers, K (where a tile lies in one block) through the
+// wave's own LDS region in whole rows; no barriers until the NW waves merge their running
+// states through LDS.
 // ---------------------------------------------------------------------------------------
 template <int HD, bool BIG, typename LdsT>
 __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
@@ -321,6 +406,9 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
   const int bs_mask = P.bs - 1;
   const size_t head_stride = (size_t)P.bs * D;  // elements per (block, head) in either pool
 
+  using SK = StreamK<HD>;
+  const u16 *kw = S.base + w * SK::ELEMS;  // this wave's K region
+  const uint32_t kw_lds = __builtin_amdgcn_readfirstlane(lds_addr_of(kw));  // wave-uniform
   const bool row_ok = r < rows;
   const int row_tok = R.tok0 + r / P.G;
   const int lim = c + row_tok;  // keys 0 .. lim are visible to this lane's row
@@ -373,22 +461,29 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
     }
     if (kt + NW < t_end) read_ids(kt + NW);
     // ---- K operand: key rows permuted so the S^T layout feeds P.V directly ------------
+    // BIG: the tile's 64 rows are contiguous in one block; whole rows go to this wave's LDS
+    // region first (read back below, once the V loads are in flight too).  Otherwise each
+    // lane loads its rows' operand chunks itself.
     bf16x8 kf[2][2][D / 32];
+    if (BIG) {
+      const u16 *kb = P.k_pool + ((size_t)blk_t * P.Hkv + R.h) * head_stride +
+                      (size_t)(k0 & bs_mask) * D;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        int key = k0 + 32 * kh + 8 * (r >> 2) + 4 * a + (r & 3);
-        int blk = blk_t;
-        if (!BIG) {
-          key = k_key(k0, kh, a);
-          blk = blk_k[kh][a];
-        }
-        const u16 *kp = P.k_pool + ((size_t)blk * P.Hkv + R.h) * head_stride +
-                        (size_t)(key & bs_mask) * D + 8 * g;
-#pragma unroll
-        for (int dc = 0; dc < D / 32; ++dc) kf[kh][a][dc] = as_bf16x8(ld16(kp + 32 * dc));
+      for (int j = 0; j < SK::NDMA; ++j) {
+        const int row = SK::RPI * j + lane / SK::CPR;
+        dma16_nt(kb + row * D + 8 * ((lane % SK::CPR) ^ swz_s<HD>(row)), kw_lds + 1024u * j);
       }
+    } else {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const u16 *kp = P.k_pool + ((size_t)blk_k[kh][a] * P.Hkv + R.h) * head_stride +
+                          (size_t)(k_key(k0, kh, a) & bs_mask) * D + 8 * g;
+#pragma unroll
+          for (int dc = 0; dc < D / 32; ++dc) kf[kh][a][dc] = as_bf16x8(ld16(kp + 32 * dc));
+        }
+    }
     // ---- V^T operand: 8 consecutive keys of one feature per lane ------------------------
     // In a block, V is stored as groups of 8 keys, each group feature-major with its 8 keys
     // adjacent (16 bytes).  One instruction (fixed kh, dt) reads, for each of the four lane
@@ -408,7 +503,23 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) vr[kh][dt] = ld16(vp[kh] + 128 * dt);
+      for (int kh = 0; kh < 2; ++kh) vr[kh][dt] = ld16_nt(vp[kh] + 128 * dt);
+    if (BIG) {
+      // The DMAs were issued before the V loads: once every load of this wave is done, the
+      // region holds the tile.  The empty asm keeps the V loads above the wait.
+      asm volatile("" ::: "memory");
+      wait_vm<0>();
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int key = 32 * kh + 8 * (r >> 2) + 4 * a + (r & 3);
+#pragma unroll
+          for (int dc = 0; dc < D / 32; ++dc)
+            kf[kh][a][dc] = *reinterpret_cast<const bf16x8 *>(
+                kw + key * D + 8 * ((4 * dc + g) ^ swz_s<HD>(key)));
+        }
+    }
     if (k0 + KT > R.khi) {  // keys at or past khi: zero V so stale bits cannot reach O
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
@@ -441,7 +552,9 @@ __device__ void stream_record(const Params &P, const Rec &R, const LdsT &S) {
 
   // ---- merge the waves through LDS ---------------------------------------------------
   // per-wave O^T dumps: wave w uses the w-th 8 KiB half-buffer of the ring (16 rows x 128
-  // floats); the running maxima and sums go to the block-id array
+  // floats); the running maxima and sums go to the block-id array.  The dumps overlap other
+  // waves' K regions, so every wave must be past its last tile first.
+  __syncthreads();
   float *so_w = reinterpret_cast<float *>(S.base + w * STAGE_K);
   float *sm = reinterpret_cast<float *>(S.ids);                // [NW][16]
   float *sl = sm + NW * STREAM_ROWS;                           // [NW][16]
@@ -505,9 +618,6 @@ static_assert(NW * stage_k(128) <= NSTAGE * stage_elems(128) &&
                   NW * stage_k(64) <= NSTAGE * stage_elems(64),
               "every wave's stream dump must fit the ring");
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
-
 // K stage: 16-byte chunk c of key row `key` sits at slot c ^ swz_k32<HD>(key).  The MFMA reads
 // of 16 lanes (rows pi(m), m = 16i .. 16i+15, one chunk) then hit 16 distinct 16-byte slots of
 // a 256-byte window: at HD 128 (256-byte rows) the swizzle takes 16 values; at HD 64 (128-byte
@@ -528,6 +638,10 @@ __device__ __forceinline__ int key_perm32(int m) {
 // The stage ring: one workgroup-shared array, stage buffer i = K [32 keys][HD] followed by
 // V [4 key groups][HD][8 keys].  Buffers are addressed as base + constant offset, so one set of per-lane
 // address registers serves every buffer.
+// The ring doubles as the stream records' per-wave K regions (128 KiB at HD 128).
+constexpr int ring_elems(int hd) {
+  return NSTAGE * stage_elems(hd) > NW * KEY_TILE * hd ? NSTAGE * stage_elems(hd) : NW * KEY_TILE * hd;
+}
 constexpr int MAX_IDS = 256;  // block ids of a tile record staged in LDS
 static_assert(2 * NW * STREAM_ROWS <= MAX_IDS, "stream merge maxima and sums must fit");
 
@@ -538,56 +652,6 @@ struct Lds {
   __device__ u16 *k(int i) const { return base + i * stage_elems(HD); }
   __device__ u16 *v(int i) const { return base + i * stage_elems(HD) + stage_k(HD); }
 };
-
-// One wave instruction: 16 bytes per lane from global memory to LDS at lds_wave_base + 16*lane.
-// Written as inline asm so that the compiler does not track these loads: its alias tracking of
-// LDS-DMA targets is easily lost and then drains every prefetched stage before ordinary LDS
-// reads.  The LDS base goes in through an "{m0}" operand, so the compiler itself writes M0 and
-// knows it is in use.  The kernel waits for the loads itself (wait_dma) and separates them from
-// LDS reads by barriers; the "memory" clobber keeps the compiler from moving memory operations
-// across them.
-__device__ __forceinline__ void dma16(const u16 *src, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "{m0}"(lds_addr)
-               : "memory");
-}
-
-// LDS byte address of a workgroup-shared array (a constant once the array is known)
-__device__ __forceinline__ uint32_t lds_addr_of(const u16 *p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const u16 *)p;
-}
-
-// Workgroup barrier for the stage ring.  __syncthreads() would also drain every vector load
-// still in flight (its fence waits for all of them), i.e. the prefetched stages; here the
-// data a stage needs is already covered by wait_dma, and LDS reads complete before their
-// MFMAs consume them, so a bare barrier suffices.  The empty asm statements keep the
-// compiler from moving memory operations across it.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// wait until at most n of this wave's LDS-DMA loads are outstanding (n in 0 .. 16)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  // s_waitcnt encoding (gfx9): vmcnt = bits 3:0 (+ bits 15:14), expcnt 6:4, lgkmcnt 11:8
-  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
-}
-__device__ __forceinline__ void wait_dma(int n) {
-  switch (n) {
-    case 0: wait_vm<0>(); break;   case 1: wait_vm<1>(); break;
-    case 2: wait_vm<2>(); break;   case 3: wait_vm<3>(); break;
-    case 4: wait_vm<4>(); break;   case 5: wait_vm<5>(); break;
-    case 6: wait_vm<6>(); break;   case 7: wait_vm<7>(); break;
-    case 8: wait_vm<8>(); break;   case 9: wait_vm<9>(); break;
-    case 10: wait_vm<10>(); break; case 11: wait_vm<11>(); break;
-    case 12: wait_vm<12>(); break; case 13: wait_vm<13>(); break;
-    case 14: wait_vm<14>(); break; case 15: wait_vm<15>(); break;
-    default: wait_vm<16>(); break;
-  }
-}
 
 // A stage is 2 * HD / 16 regions of 1 KiB: K regions first (HD / 16 of them, key rows of 2*HD
 // bytes), then V regions (64 consecutive 16-byte (key group, feature) runs each: the stage's V
@@ -977,7 +1041,7 @@ __device__ void tile_record(const Params &P, const Rec &R, const Lds<HD> &S) {
 // BSC: 0 = blocks of < 32 keys, 1 = blocks of 32 keys, 2 = blocks of >= 64 keys.
 template <int HD, int BSC>
 __global__ __launch_bounds__(NT, WG_PER_CU) void attention_bf16_kernel(Params P) {
-  __shared__ __attribute__((aligned(16))) u16 ring[NSTAGE * stage_elems(HD)];
+  __shared__ __attribute__((aligned(16))) u16 ring[ring_elems(HD)];
   __shared__ int blk_ids[MAX_IDS];
   const Rec R = load_rec<HD>(P, blockIdx.x);
   if (R.s < 0 || !rec_fits_workspace<HD>(P, R)) return;  // never write outside the workspace
