@@ -18,13 +18,14 @@ from ragged_blocked_kv_splitfuse_amd import fg
 from ragged_blocked_kv_splitfuse_amd.runtime import stream_handle
 from ragged_blocked_kv_splitfuse_amd.workloads import f32_to_bf16_bits
 
-SHAPES = [  # (T, K, N): LLaMA-2-7B q/k/v/o (4096 -> 4096), Mistral-7B k/v (4096 -> 1024); the
-    # token counts reach each kernel the GEMM picks (the weight-streaming kernel with 1 to 4
-    # 16-token tiles up to 64 rows; 64, 128 and 256-row tiles above), with ragged tails, and
-    # N = 1536 the tile placement without the per-XCD split
+SHAPES = [  # (T, K, N): LLaMA-2-7B q/k/v/o (4096 -> 4096), Mistral-7B k/v (4096 -> 1024), a
+    # fused QKV width (12288); the token counts reach each kernel the GEMM picks (the
+    # weight-streaming kernel with 1 to 4 16-token tiles up to 64 rows; 64, 128 and 256-row
+    # tiles above, 256 x 256 at T = 1174, N = 12288), with ragged tails, and N = 1536 the tile
+    # placement without the per-XCD split
     (1, 4096, 4096), (17, 4096, 4096), (22, 4096, 1024), (37, 4096, 4096), (64, 4096, 1024),
     (512, 4096, 1024), (2048, 4096, 4096), (3000, 4096, 1024), (4100, 4096, 4096),
-    (300, 512, 1536),
+    (1174, 4096, 12288), (300, 512, 1536),
 ]
 
 
