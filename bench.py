@@ -341,6 +341,7 @@ def main():
         "roofline": roof,
         "per_config": per_config,
         "hbm_reference": hbm_reference(append_bytes=append_bytes) if args.per_config else None,
+        "mfma_reference": mfma_reference() if args.per_config else None,
         "kernels": {"attention_us": t_attn * 1e6, "kv_append_us": t_app * 1e6,
                     "kv_append_GBps": append_bytes / t_app / 1e9,
                     "gpu_only_tokens_per_s": T / (t_attn + t_app),
@@ -560,6 +561,36 @@ def hbm_reference(gib=4, reps=10, append_bytes=0):
                   f"{2 * gib} GiB of fp32 (read bytes), {reps} repetitions each" +
                   ("; a copy moving kv_append's bytes after 1 GiB of other traffic, median of 20"
                    if append_bytes else ""))
+    return out
+
+
+def mfma_reference(sizes=(8192, 16384), flops_per_size=2e13):
+    """Practical bf16 matrix-core rate on this device, measured beside the pass: torch's own
+    (vendor library) bf16 GEMM on square n x n x n problems, timed with events over enough
+    repetitions for ~`flops_per_size` flops each after 3 warm-ups.  A plain GEMM has no
+    softmax, no masking and no gathers, so this is the rate an MFMA-bound attention pass
+    could at best approach on this part, against the published 2.5 PFLOP/s."""
+    import torch
+    out = {}
+    for n in sizes:
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            c = a @ b
+        reps = max(3, int(flops_per_size / (2 * n ** 3)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        tf = 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        out[f"gemm_{n}_TFLOPs"] = tf
+        out[f"gemm_{n}_frac_of_peak"] = tf / BF16_PEAK_TFLOPS
+        del a, b, c
+    torch.cuda.empty_cache()
+    out["how"] = (f"torch bf16 matmul, square sizes {list(sizes)}, event-timed, "
+                  f"~{flops_per_size:.0e} flops each after 3 warm-ups")
     return out
 
 
