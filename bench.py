@@ -489,7 +489,16 @@ def roofline(w, workload, attn_bytes, attn_flops, t_attn):
     roof["algorithmic_bytes"] = attn_bytes
     roof["algorithmic_flops"] = attn_flops
     roof["mfma_frac"] = attn_flops / t_attn / 1e12 / BF16_PEAK_TFLOPS
+    if w.dtype == "bf16":
+        roof.update(bound_fracs(attn_bytes, attn_flops, t_attn))
     return roof
+
+
+def bound_fracs(B, F, t):
+    """Roofline time over measured time for both combinations of the two bounds: the larger of
+    bytes / HBM peak and flops / MFMA peak, and their sum (the time if the two never overlap)."""
+    tb, tf = B / (HBM_PEAK_GBS * 1e9), F / (BF16_PEAK_TFLOPS * 1e12)
+    return {"max_bound_frac": max(tb, tf) / t, "additive_bound_frac": (tb + tf) / t}
 
 
 def config_entry(w, r, bound):
@@ -509,7 +518,8 @@ def config_entry(w, r, bound):
             "mfma_frac": mfma, "kv_append_hbm_frac": r["append_bytes"] / t_app / 1e9 / HBM_PEAK_GBS,
             "gpu_only_tokens_per_s": r["T"] / (t_attn + t_app),
             "step_tokens_per_s": r["T"] * len(r["host_s"]) / r["elapsed"],
-            "split_groups": int(r["info"].num_groups), "work_records": int(r["info"].num_work)}
+            "split_groups": int(r["info"].num_groups), "work_records": int(r["info"].num_work),
+            **bound_fracs(B, F, t_attn)}
 
 
 def hbm_reference(gib=4, reps=10, append_bytes=0):

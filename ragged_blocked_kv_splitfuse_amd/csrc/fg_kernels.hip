@@ -275,35 +275,60 @@ constexpr int merge_rows(int hd) { return NT / (hd / 8); }  // rows one merge wo
 // Combine: the merge record of a split group reads every split's (m, l, acc) partial in
 // split order (deterministic) and writes O.  Runs in its own launch after the main kernel.
 // Each workgroup merges one MERGE_ROWS-row slice (blockIdx.y) of the group: one thread per (row,
-// 8-feature chunk).
+// 8-feature chunk).  The partials of up to MERGE_BATCH splits are requested together, so a
+// group costs about one memory latency per batch rather than one per split; the sums still
+// run in split order.
+constexpr int MERGE_BATCH = 4;
+
 template <int HD>
 __device__ void merge_splits(const Params &P, const Rec &R) {
   constexpr int D = HD;
   constexpr int MERGE_ROWS = merge_rows(HD);
+  constexpr int KB = MERGE_BATCH;
   const int64_t slot = slot_floats(R.mode, D);
   const int cap = R.mode == MODE_STREAM ? STREAM_ROWS : TILE_ROWS;
   const int rows = R.ntok * P.G;
   const int qs = ldc(P.query_start, R.s);
-  {
-    const int row = MERGE_ROWS * blockIdx.y + threadIdx.x / (D / 8), chunk = threadIdx.x % (D / 8);
-    if (row >= rows) return;
-    float M = NEG_INF;
-    for (int k = 0; k < R.nsplit; ++k) M = fmaxf(M, P.ws[R.poff + k * slot + cap * D + row]);
-    float L = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int k = 0; k < R.nsplit; ++k) {
-      const float *sp = P.ws + R.poff + k * slot;
-      const float m = sp[cap * D + row];
-      const float f = (m == NEG_INF) ? 0.f : fast_exp2(m - M);
-      L += sp[cap * D + cap + row] * f;
-      const float4 a = *reinterpret_cast<const float4 *>(sp + row * D + chunk * 8);
-      const float4 b = *reinterpret_cast<const float4 *>(sp + row * D + chunk * 8 + 4);
-      o[0] += a.x * f; o[1] += a.y * f; o[2] += a.z * f; o[3] += a.w * f;
-      o[4] += b.x * f; o[5] += b.y * f; o[6] += b.z * f; o[7] += b.w * f;
-    }
-    const int t = qs + R.tok0 + row / P.G;
-    const int head = R.h * P.G + row % P.G;
-    if (t < P.num_tokens) store_out8<HD>(P, t, head, chunk * 8, o, 1.f / L);
+  const int row = MERGE_ROWS * blockIdx.y + threadIdx.x / (D / 8), chunk = threadIdx.x % (D / 8);
+  if (row >= rows) return;
+  const float *base = P.ws + R.poff;
+  const int ns = R.nsplit;
+  float M = NEG_INF;
+  for (int k0 = 0; k0 < ns; k0 += KB) {
+    float mv[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      mv[j] = (k0 + j < ns) ? base[(int64_t)(k0 + j) * slot + cap * D + row] : NEG_INF;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) M = fmaxf(M, mv[j]);
   }
+  float L = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int k0 = 0; k0 < ns; k0 += KB) {
+    float mv[KB], lv[KB];
+    float4 av[KB], bv[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (k0 + j < ns) {
+        const float *sp = base + (int64_t)(k0 + j) * slot;
+        mv[j] = sp[cap * D + row];
+        lv[j] = sp[cap * D + cap + row];
+        av[j] = *reinterpret_cast<const float4 *>(sp + row * D + chunk * 8);
+        bv[j] = *reinterpret_cast<const float4 *>(sp + row * D + chunk * 8 + 4);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (k0 + j < ns) {
+        const float f = (mv[j] == NEG_INF) ? 0.f : fast_exp2(mv[j] - M);
+        L += lv[j] * f;
+        o[0] += av[j].x * f; o[1] += av[j].y * f; o[2] += av[j].z * f; o[3] += av[j].w * f;
+        o[4] += bv[j].x * f; o[5] += bv[j].y * f; o[6] += bv[j].z * f; o[7] += bv[j].w * f;
+      }
+    }
+  }
+  const int t = qs + R.tok0 + row / P.G;
+  const int head = R.h * P.G + row % P.G;
+  if (t < P.num_tokens) store_out8<HD>(P, t, head, chunk * 8, o, 1.f / L);
 }
 
 // One wave instruction: 16 bytes per lane from global memory to LDS at lds_wave_base + 16*lane.
