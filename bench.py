@@ -240,10 +240,13 @@ def time_pass(S, steps, warmup):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_total + n_app)]
     timed_attn = []
-    host_s = []
+    host_s = []   # host work per step (compose, plan, upload, launches)
+    wait_s = []   # per step, time the host waited for a free descriptor buffer (flow control:
+                  # the ring lets the host run 8 steps ahead of the GPU, then it waits)
 
     def step(i, time_append=False):
         t0 = time.perf_counter()
+        w0 = desc.wait_s
         info, work = compose_and_plan()
         c = desc.upload(hb, work, stream, record=False)
         mark = not time_append and (i % 4 == 3 or i == n_total - 1)
@@ -263,7 +266,9 @@ def time_pass(S, steps, warmup):
         if mark or time_append:
             desc.release(ev[i][1])
         restore_free_list()
-        host_s.append(time.perf_counter() - t0)
+        waited = desc.wait_s - w0
+        host_s.append(time.perf_counter() - t0 - waited)
+        wait_s.append(waited)
         return info
 
     for i in range(warmup):
@@ -284,7 +289,8 @@ def time_pass(S, steps, warmup):
     return dict(info=info, T=T, nseq=nseq, nq=nq, ctx=ctx, kv_tokens=kv_tokens,
                 attn_bytes=attn_bytes, attn_flops=attn_flops, append_bytes=append_bytes,
                 t_attn=float(np.mean(attn_ms)) * 1e-3, t_app=float(np.mean(app_ms)) * 1e-3,
-                elapsed=t1 - t0, q=q, k_new=k_new, v_new=v_new, host_s=host_s[warmup:n_total])
+                elapsed=t1 - t0, q=q, k_new=k_new, v_new=v_new, host_s=host_s[warmup:n_total],
+                wait_s=wait_s[warmup:n_total])
 
 
 def main():
@@ -345,7 +351,8 @@ def main():
         "kernels": {"attention_us": t_attn * 1e6, "kv_append_us": t_app * 1e6,
                     "kv_append_GBps": append_bytes / t_app / 1e9,
                     "gpu_only_tokens_per_s": T / (t_attn + t_app),
-                    "host_us_per_step": float(np.mean(host_s)) * 1e6},
+                    "host_us_per_step": float(np.mean(host_s)) * 1e6,
+                    "host_wait_us_per_step": float(np.mean(r["wait_s"])) * 1e6},
         "cpu_baseline": cpu_baseline(args, w, cache, hb, q, k_new, v_new) if args.cpu_seconds > 0 else None,
     }
     print(json.dumps(result), flush=True)

@@ -12,6 +12,7 @@ No arithmetic of the method happens here.
 from __future__ import annotations
 
 import ctypes
+import time
 
 import numpy as np
 import torch
@@ -91,6 +92,7 @@ class DeviceDescriptors:
         self.cstruct = fg.FgRaggedBatch()
         self.work_ptr = 0
         self._pending = []  # slots uploaded with record=False and not yet released
+        self.wait_s = 0.0   # host seconds spent waiting for a staging buffer to come free
 
     def _staging(self, n):
         i = self.slot
@@ -99,7 +101,9 @@ class DeviceDescriptors:
             raise RuntimeError("descriptor ring reused before release(): call release() at "
                                "least once every ring uploads")
         if self.events[i] is not None:
+            t0 = time.perf_counter()
             self.events[i].synchronize()        # the copy that last read this buffer is done
+            self.wait_s += time.perf_counter() - t0
         if self.ring[i] is None or self.ring[i].numel() < n:
             self.ring[i] = torch.empty(max(n, 1024), dtype=torch.int32, pin_memory=True)
         return i, self.ring[i]
