@@ -319,6 +319,7 @@ def main():
     attn_bytes, attn_flops, append_bytes = r["attn_bytes"], r["attn_flops"], r["append_bytes"]
     t_attn, t_app, elapsed = r["t_attn"], r["t_app"], r["elapsed"]
     q, k_new, v_new, host_s = r["q"], r["k_new"], r["v_new"], r["host_s"]
+    wait_s = r["wait_s"]
     value = T * args.steps / elapsed
 
     roof = roofline(w, args.workload, attn_bytes, attn_flops, t_attn)
@@ -352,7 +353,7 @@ def main():
                     "kv_append_GBps": append_bytes / t_app / 1e9,
                     "gpu_only_tokens_per_s": T / (t_attn + t_app),
                     "host_us_per_step": float(np.mean(host_s)) * 1e6,
-                    "host_wait_us_per_step": float(np.mean(r["wait_s"])) * 1e6},
+                    "host_wait_us_per_step": float(np.mean(wait_s)) * 1e6},
         "cpu_baseline": cpu_baseline(args, w, cache, hb, q, k_new, v_new) if args.cpu_seconds > 0 else None,
     }
     print(json.dumps(result), flush=True)
