@@ -65,6 +65,15 @@ CASES = {
     "steep_logits_split": (dict(hq=4, hkv=4, bs=32, budget=200, n_decode=3,
                                 decode_ctx=(800, 2000), prompts=((1000, 1200),), q_scale=40.0),
                            100000),
+    # planned for one compute unit, so no key range is split: tile records then span more
+    # block ids (291 at block size 32, 268 at 64) than the kernel stages in LDS, and read
+    # them from the table instead; the decode records stream ~9000 keys unsplit
+    "ids_beyond_lds_bs32": (dict(hq=4, hkv=4, bs=32, budget=300, n_decode=2,
+                                 decode_ctx=(9000, 9500), prompts=((9000, 9300),)), 1),
+    "ids_beyond_lds_bs64": (dict(hq=4, hkv=2, bs=64, budget=200, n_decode=1,
+                                 decode_ctx=(100, 200), prompts=((17000, 17150),)), 1),
+    "ids_beyond_lds_hd64": (dict(hq=8, hkv=2, d=64, bs=64, budget=160, n_decode=1,
+                                 decode_ctx=(100, 200), prompts=((17000, 17100),)), 1),
 }
 
 
