@@ -295,6 +295,19 @@ fg_status fg_ragged_attention_noalloc(const fg_cache *cache, const fg_ragged_bat
 fg_status fg_linear_bf16(const void *x, const void *w, void *y, int32_t T, int32_t K, int32_t N,
                          void *stream);
 
+/* The fused QKV projection (same paper card, "Key points": the FasterTransformer layer kernels):
+ * one product over the stacked weights w_qkv[Nq + 2*Nkv][K] (Wq's Nq rows, then Wk's Nkv rows,
+ * then Wv's) whose output columns land in three separate dense matrices, q[T][Nq], k[T][Nkv]
+ * and v[T][Nkv] -- the layouts fg_ragged_attention and fg_kv_append read (Nq = query heads x
+ * head dim, Nkv = KV heads x head dim).  Each output element equals the corresponding
+ * fg_linear_bf16 output of that weight block, bit for bit (same kernels and summation order);
+ * one launch instead of three gives the tile chooser a wider product.  Same memory and
+ * arithmetic rules as fg_linear_bf16; allocates nothing.  Errors: FG_E_ARG (null or unaligned
+ * pointer, T < 0, K, Nq or Nkv < 1), FG_E_UNSUPPORTED (Nq or Nkv not a multiple of 128, K not
+ * a multiple of 64), FG_E_HIP.  T = 0 does nothing. */
+fg_status fg_linear_qkv_bf16(const void *x, const void *w_qkv, void *q, void *k, void *v,
+                             int32_t T, int32_t K, int32_t Nq, int32_t Nkv, void *stream);
+
 const char *fg_status_string(fg_status status);
 const char *fg_last_error(void);
 

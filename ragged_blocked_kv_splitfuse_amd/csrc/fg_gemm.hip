@@ -6,9 +6,10 @@
 //     y[T][N] = x[T][K] . w[N][K]^T        (w in the [out][in] layout of a linear layer)
 // with bf16 inputs, fp32 accumulation and one round-to-nearest-even to bf16 per output.
 //
-// Design (CDNA4): a workgroup of four waves (2 x 2) computes a (64*TT tokens) x (64*FT
-// features) tile; each wave owns FT x TT tiles of the 32x32x16 bf16 MFMA (up to 4 x 4, whose
-// 256 accumulators per lane live in AGPRs, one wave per SIMD).  The MFMA computes the
+// Design (CDNA4): a workgroup of WF x WT waves computes a (32*TT*WT tokens) x (32*FT*WF
+// features) tile; each wave owns FT x TT tiles of the 32x32x16 bf16 MFMA.  Four-wave tiles run
+// two workgroups per CU; the 256 x 256 tile is eight waves (4 x 2, 2 x 4 MFMA tiles each), so
+// that every SIMD has two waves to issue its matrix instructions from.  The MFMA computes the
 // transposed product C^T = W . X^T (A operand: 32 weight rows, B operand: 32 token rows; both
 // rows are contiguous along K, so every operand is one 16-byte load), which leaves each lane
 // with runs of four consecutive output features of one token: 8-byte stores of y rows.  The
@@ -36,37 +37,56 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
-constexpr int GT = 256;    // threads: four waves, 2 x 2 over the tile
 constexpr int NUM_XCD = 8;
 
-template <int FT, int TT, int BK>
+// WF x WT waves over the workgroup's tile (wave-major along tokens), each owning FT x TT tiles
+// of the 32x32x16 MFMA.
+template <int FT, int TT, int BK, int WF, int WT>
 struct Tile {
-  static constexpr int BN = 64 * FT;                 // output features per workgroup
-  static constexpr int BM = 64 * TT;                 // tokens per workgroup
+  static constexpr int NWV = WF * WT;                // waves per workgroup
+  static constexpr int THREADS = 64 * NWV;
+  static constexpr int BN = 32 * FT * WF;            // output features per workgroup
+  static constexpr int BM = 32 * TT * WT;            // tokens per workgroup
   static constexpr int ROW = BK * 2;                 // bytes per tile row of a stage
   static constexpr int CH = BK / 8;                  // 16-byte chunks per row
   static constexpr int STAGE = (BN + BM) * ROW;      // weight rows, then token rows
   static constexpr int REGIONS = STAGE / 1024;       // 1 KiB per LDS-DMA wave instruction
   static constexpr int W_REGIONS = BN * ROW / 1024;  // regions of weight rows
   static constexpr int RPR = 1024 / ROW;             // rows per region
-  static constexpr int DPW = REGIONS / 4;            // LDS-DMA instructions per wave and stage
-  // Workgroups per compute unit: 4 x 4 MFMA tiles per wave keep 256 accumulators per lane (in
-  // AGPRs), which leaves room for one wave per SIMD; smaller tiles run two workgroups per CU.
-  static constexpr int WGS = FT * TT >= 16 ? 1 : 2;
+  static constexpr int DPW = REGIONS / NWV;          // LDS-DMA instructions per wave and stage
+  // Workgroups per compute unit: eight waves (two per SIMD) fill a CU alone; four-wave tiles
+  // run two workgroups per CU.
+  static constexpr int WGS = NWV == 8 ? 1 : 2;
   // ring depth: three stages where the workgroups of a compute unit still fit in LDS, else two
   static constexpr int LDS_PER_WG = (WGS == 1 ? 144 : 80) * 1024;
   static constexpr int NSTG = 3 * STAGE <= LDS_PER_WG ? 3 : 2;
-  static_assert(DPW * 4 == REGIONS && W_REGIONS * 1024 == BN * ROW, "regions");
+  static_assert(DPW * NWV == REGIONS && W_REGIONS * 1024 == BN * ROW, "regions");
+  static_assert(3 * DPW <= 63, "the stage waits count LDS-DMA loads in vmcnt's range");
   static_assert(NSTG * STAGE <= LDS_PER_WG, "the ring must fit the workgroups of a CU");
 };
 
 // 16-byte chunk c of tile row r sits at slot c ^ swz(r): the 16 lanes of one operand read (16
 // consecutive rows, one chunk) then hit 16 distinct 16-byte slots of a 256-byte window.  Rows
-// of 64 bytes (BK 32): four rows per window, the swizzle takes 4 values; rows of 128 bytes
-// (BK 64): two rows per window, 8 values.
+// of 128 bytes (BK 64): two rows per window, the swizzle takes 8 values.
 template <int BK>
 __device__ __forceinline__ int swz(int r) {
-  return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7;
+  static_assert(BK == 64, "stages are 64 inner elements wide");
+  return (r >> 1) & 7;
+}
+
+// Where the product's output columns go: columns [col0[s], col0[s + 1]) form row-major matrix
+// s, y[s][T][col0[s + 1] - col0[s]] (one matrix for a plain linear layer; Q, K and V for the
+// fused QKV projection).  Every boundary is a multiple of the tile widths in use, so the
+// columns a workgroup writes lie in one matrix.
+struct OutSeg {
+  u16 *y[3];
+  int col0[4];  // col0[0] = 0; unused boundaries equal N
+};
+
+// element (t, f) of the output, f a column of the whole product
+__device__ __forceinline__ u16 *out_at(const OutSeg &o, int t, int f) {
+  const int s = (f >= o.col0[1]) + (f >= o.col0[2]);
+  return o.y[s] + (size_t)t * (o.col0[s + 1] - o.col0[s]) + (f - o.col0[s]);
 }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -92,13 +112,14 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int FT, int TT, int BK>
-__global__ __launch_bounds__(GT, FT * TT >= 16 ? 1 : 2) void gemm_nt_bf16_kernel(const u16 *__restrict__ x,
+template <int FT, int TT, int BK, int WF, int WT>
+__global__ __launch_bounds__(64 * WF * WT, WF * WT == 8 ? 1 : 2) void gemm_nt_bf16_kernel(const u16 *__restrict__ x,
                                                              const u16 *__restrict__ w,
-                                                             u16 *__restrict__ y, int T, int K,
+                                                             const OutSeg o, int T, int K,
                                                              int N, int xcd_split) {
-  using Tl = Tile<FT, TT, BK>;
+  using Tl = Tile<FT, TT, BK, WF, WT>;
   constexpr int BN = Tl::BN, BM = Tl::BM, ROW = Tl::ROW, DPW = Tl::DPW, NSTG = Tl::NSTG;
+  constexpr int NWV = Tl::NWV;
   __shared__ __attribute__((aligned(16))) unsigned char ring[NSTG * Tl::STAGE];
   const int NT = N / BN;
   int mt, nt;
@@ -113,15 +134,15 @@ __global__ __launch_bounds__(GT, FT * TT >= 16 ? 1 : 2) void gemm_nt_bf16_kernel
   }
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wf = wv >> 1, wt = wv & 1;  // this wave's features (wf) and tokens (wt)
+  const int wf = wv / WT, wt = wv % WT;  // this wave's features (wf) and tokens (wt)
   const int f_base = nt * BN, t_base = mt * BM;
 
-  // LDS-DMA sources of this lane: wave wv fills regions p*4 + wv; a region is RPR tile rows
+  // LDS-DMA sources of this lane: wave wv fills regions p*NWV + wv; a region is RPR tile rows
   // (weight rows first, then token rows), lane -> (row, 16-byte slot)
   const u16 *src[DPW];
 #pragma unroll
   for (int p = 0; p < DPW; ++p) {
-    const int reg = p * 4 + wv;
+    const int reg = p * NWV + wv;
     const bool wrow = reg < Tl::W_REGIONS;
     const int rr = Tl::RPR * (wrow ? reg : reg - Tl::W_REGIONS) + lane / Tl::CH;
     const int c = (lane % Tl::CH) ^ swz<BK>(rr);
@@ -135,7 +156,7 @@ __global__ __launch_bounds__(GT, FT * TT >= 16 ? 1 : 2) void gemm_nt_bf16_kernel
   auto issue = [&](int s) {  // stage s into buffer s % NSTG
     const uint32_t base = lds0 + (uint32_t)(s % NSTG) * Tl::STAGE;
 #pragma unroll
-    for (int p = 0; p < DPW; ++p) dma16(src[p] + (size_t)s * BK, base + 1024u * (p * 4 + wv));
+    for (int p = 0; p < DPW; ++p) dma16(src[p] + (size_t)s * BK, base + 1024u * (p * NWV + wv));
   };
 
   // operand rows of this lane: weights 32*FT*wf + 32*i + n, tokens 32*TT*wt + 32*j + n
@@ -227,7 +248,7 @@ __global__ __launch_bounds__(GT, FT * TT >= 16 ? 1 : 2) void gemm_nt_bf16_kernel
   for (int j = 0; j < TT; ++j) {
     const int t = t_base + 32 * TT * wt + 32 * j + n;
     if (t >= T) continue;
-    u16 *yr = y + (size_t)t * N + f_base + 32 * FT * wf + 4 * g;
+    u16 *yr = out_at(o, t, f_base + 32 * FT * wf + 4 * g);
 #pragma unroll
     for (int i = 0; i < FT; ++i)
 #pragma unroll
@@ -240,11 +261,12 @@ __global__ __launch_bounds__(GT, FT * TT >= 16 ? 1 : 2) void gemm_nt_bf16_kernel
   }
 }
 
-template <int FT, int TT, int BK>
-void launch(const u16 *x, const u16 *w, u16 *y, int T, int K, int N, hipStream_t st) {
-  using Tl = Tile<FT, TT, BK>;
+template <int FT, int TT, int BK, int WF, int WT>
+void launch(const u16 *x, const u16 *w, const OutSeg &y, int T, int K, int N, hipStream_t st) {
+  using Tl = Tile<FT, TT, BK, WF, WT>;
   const int NT = N / Tl::BN, MT = (T + Tl::BM - 1) / Tl::BM;
-  hipLaunchKernelGGL((gemm_nt_bf16_kernel<FT, TT, BK>), dim3((unsigned)(NT * MT)), dim3(GT), 0,
+  hipLaunchKernelGGL((gemm_nt_bf16_kernel<FT, TT, BK, WF, WT>), dim3((unsigned)(NT * MT)),
+                     dim3(Tl::THREADS), 0,
                      st, x, w, y, T, K, N, NT % NUM_XCD == 0 ? 1 : 0);
 }
 
@@ -289,7 +311,7 @@ struct Skinny {
 template <int NT>
 __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_bf16_kernel(const u16 *__restrict__ x,
                                                                        const u16 *__restrict__ w,
-                                                                       u16 *__restrict__ y, int T,
+                                                                       const OutSeg o, int T,
                                                                        int K, int N) {
   using Sk = Skinny<NT>;
   constexpr int ROWB = Sk::ROWB, DPW = Sk::DPW, NSTG = Sk::NSTG;
@@ -360,16 +382,58 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_bf16_kernel(const u16 
       bf16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (__bf16)sum[e];
-      *reinterpret_cast<bf16x4 *>(y + (size_t)t * N + f0 + 4 * (l >> 4)) = v;
+      *reinterpret_cast<bf16x4 *>(out_at(o, t, f0 + 4 * (l >> 4))) = v;
     }
   }
 }
 
 template <int NT>
-void launch_skinny(const u16 *x, const u16 *w, u16 *y, int T, int K, int N, hipStream_t st) {
+void launch_skinny(const u16 *x, const u16 *w, const OutSeg &y, int T, int K, int N,
+                   hipStream_t st) {
   hipLaunchKernelGGL((gemm_skinny_bf16_kernel<NT>), dim3((unsigned)(N / 16)), dim3(SK_THREADS),
                      0, st, x, w, y, T, K, N);
 }
+
+// Picks the kernel and tile for T x N x K and launches it.  wide_ok: every output matrix's
+// width is a multiple of 256 (the 256 x 256 tile may be used).
+fg_status run_linear(const u16 *xp, const u16 *wp, const OutSeg &o, int T, int K, int N,
+                     bool wide_ok, hipStream_t st) {
+  // 256 x 256 tiles (eight waves, 64-wide stages, one workgroup per compute unit, the chip has
+  // 256) when there are at least ~140 of them in every round, the last included, and their
+  // token rows are at least 90% used; else 128 x 128 tiles (four waves, two workgroups per CU)
+  // when they put at least one workgroup on every CU; else 128 x 64 tiles.
+  // Measured on the projection shapes (K 4096; N 12288, 6144 and 4096; T 512 to 4100): the
+  // eight-wave 256 x 256 tiles run 3-13% faster than 128 x 128 from 144 workgroups on when
+  // every round is full, but lose 5-15% where the last round is partly empty and ~40% at
+  // T = 640 (a last token tile half empty); the four-wave 256 x 256 form they replace (one
+  // wave per SIMD) was 7-16% slower than them, and 256 x 128 tiles are now slower than
+  // 128 x 128 everywhere.  128 x 64 tiles win at up to 256 128 x 128 workgroups (one round
+  // of two per CU) and lose ~20% just above (a second round).
+  // Up to 64 token rows: the weight-streaming kernel (whole stages of 512 or 256 inner
+  // elements).
+  if (T <= 64 && K % 512 == 0) {
+    if (T <= 16) launch_skinny<1>(xp, wp, o, T, K, N, st);
+    else if (T <= 32) launch_skinny<2>(xp, wp, o, T, K, N, st);
+    else if (T <= 48) launch_skinny<3>(xp, wp, o, T, K, N, st);
+    else launch_skinny<4>(xp, wp, o, T, K, N, st);
+  } else {
+    const auto tiles = [&](int bm, int bn) { return (int64_t)((T + bm - 1) / bm) * (N / bn); };
+    constexpr int64_t CUS = 256, FULL = 140;
+    const int64_t t256 = wide_ok ? tiles(256, 256) : 0, rem = t256 % CUS;
+    const bool rows_used = 10 * (int64_t)T >= 9 * (int64_t)((T + 255) / 256 * 256);
+    if (t256 >= FULL && (rem == 0 || rem >= FULL) && rows_used)
+      launch<2, 4, 64, 4, 2>(xp, wp, o, T, K, N, st);
+    else if (tiles(128, 128) > CUS)
+      launch<2, 2, 64, 2, 2>(xp, wp, o, T, K, N, st);
+    else
+      launch<2, 1, 64, 2, 2>(xp, wp, o, T, K, N, st);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FG_E_HIP, "GEMM launch: %s", hipGetErrorString(e));
+  return FG_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
 
@@ -379,47 +443,46 @@ extern "C" fg_status fg_linear_bf16(const void *x, const void *w, void *y, int32
   if (T < 0 || K < 1 || N < 1) return fail(FG_E_ARG, "sizes T=%d K=%d N=%d", T, K, N);
   if (T == 0) return FG_OK;
   if (!x || !w || !y) return fail(FG_E_ARG, "null x, w or y");
-  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) |
-       reinterpret_cast<uintptr_t>(y)) & 15)
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y))
     return fail(FG_E_ARG, "x, w and y must be 16-byte aligned");
   if (N % 128 || K % 64)
     return fail(FG_E_UNSUPPORTED, "the GEMM tiles need N %% 128 == 0 and K %% 64 == 0 (N=%d, K=%d)",
                 N, K);
   if ((int64_t)T * (N / 128) > INT32_MAX) return fail(FG_E_UNSUPPORTED, "too many tiles");
-  const u16 *xp = (const u16 *)x, *wp = (const u16 *)w;
-  u16 *yp = (u16 *)y;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // 256 x 256 tiles (64-wide stages, one workgroup per compute unit, the chip has 256) when
-  // every round of workgroups, the last one included, fills at least ~200 of the CUs; else the
-  // largest other tile that still gives well over one workgroup per compute unit, else the
-  // smallest.
-  // Measured on the projection shapes (K 4096; N 12288, 6144 and 4096; T 512 to 4096):
-  // 256 x 256 tiles gain 10-20% at 240 and 768 workgroups, lose ~10-14% at 384 (a half-empty
-  // last round) and ~25-60% below 200 workgroups; 256 x 128 tiles pay from 512 workgroups on,
-  // 128 x 128 tiles from ~300.
-  // Up to 64 token rows: the weight-streaming kernel (whole stages of 512 or 256 inner
-  // elements).
-  if (T <= 64 && K % 512 == 0) {
-    if (T <= 16) launch_skinny<1>(xp, wp, yp, T, K, N, st);
-    else if (T <= 32) launch_skinny<2>(xp, wp, yp, T, K, N, st);
-    else if (T <= 48) launch_skinny<3>(xp, wp, yp, T, K, N, st);
-    else launch_skinny<4>(xp, wp, yp, T, K, N, st);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(FG_E_HIP, "GEMM launch: %s", hipGetErrorString(e));
-    return FG_OK;
-  }
-  const auto tiles = [&](int bm, int bn) { return (int64_t)((T + bm - 1) / bm) * (N / bn); };
-  constexpr int64_t WANT = 300, CUS = 256, FULL = 200;
-  const int64_t t44 = N % 256 == 0 ? tiles(256, 256) : 0, rem = t44 % CUS;
-  if (t44 >= FULL && (rem == 0 || rem >= FULL))
-    launch<4, 4, 64>(xp, wp, yp, T, K, N, st);
-  else if (N % 256 == 0 && tiles(128, 256) >= 512)
-    launch<4, 2, 32>(xp, wp, yp, T, K, N, st);
-  else if (tiles(128, 128) >= WANT)
-    launch<2, 2, 64>(xp, wp, yp, T, K, N, st);
-  else
-    launch<2, 1, 64>(xp, wp, yp, T, K, N, st);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(FG_E_HIP, "GEMM launch: %s", hipGetErrorString(e));
-  return FG_OK;
+  OutSeg o;
+  o.y[0] = o.y[1] = o.y[2] = (u16 *)y;
+  o.col0[0] = 0;
+  o.col0[1] = o.col0[2] = o.col0[3] = N;
+  return run_linear((const u16 *)x, (const u16 *)w, o, T, K, N, N % 256 == 0,
+                    reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" fg_status fg_linear_qkv_bf16(const void *x, const void *w_qkv, void *q, void *k,
+                                        void *v, int32_t T, int32_t K, int32_t Nq, int32_t Nkv,
+                                        void *stream) {
+  fgi::clear_error();
+  if (T < 0 || K < 1 || Nq < 1 || Nkv < 1)
+    return fail(FG_E_ARG, "sizes T=%d K=%d Nq=%d Nkv=%d", T, K, Nq, Nkv);
+  if (T == 0) return FG_OK;
+  if (!x || !w_qkv || !q || !k || !v) return fail(FG_E_ARG, "null x, w_qkv, q, k or v");
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(FG_E_ARG, "x, w_qkv, q, k and v must be 16-byte aligned");
+  if (Nq % 128 || Nkv % 128 || K % 64)
+    return fail(FG_E_UNSUPPORTED,
+                "the GEMM tiles need Nq and Nkv multiples of 128 and K %% 64 == 0 "
+                "(Nq=%d, Nkv=%d, K=%d)", Nq, Nkv, K);
+  const int64_t N64 = (int64_t)Nq + 2 * (int64_t)Nkv;
+  if (N64 > INT32_MAX / 2 || (int64_t)T * (N64 / 128) > INT32_MAX)
+    return fail(FG_E_UNSUPPORTED, "too many tiles");
+  const int N = (int)N64;
+  OutSeg o;
+  o.y[0] = (u16 *)q;
+  o.y[1] = (u16 *)k;
+  o.y[2] = (u16 *)v;
+  o.col0[0] = 0;
+  o.col0[1] = Nq;
+  o.col0[2] = Nq + Nkv;
+  o.col0[3] = N;
+  return run_linear((const u16 *)x, (const u16 *)w_qkv, o, T, K, N, Nq % 256 == 0 && Nkv % 256 == 0,
+                    reinterpret_cast<hipStream_t>(stream));
 }

@@ -29,6 +29,7 @@ EXPORTS = [
     "fg_splitfuse_commit", "fg_splitfuse_retire", "fg_validate_batch", "fg_validate_work",
     "fg_kv_append", "fg_attention_plan", "fg_ragged_attention_workspace_size",
     "fg_ragged_attention", "fg_ragged_attention_noalloc", "fg_linear_bf16",
+    "fg_linear_qkv_bf16",
     "fg_status_string", "fg_last_error",
 ]
 FG_NOALLOC_WORKSPACE_BYTES = 64 << 20   # include/fg.h
@@ -125,6 +126,8 @@ def _declare(L):
                                          ctypes.POINTER(FgPlanInfo), vp, vp, ctypes.c_int32,
                                          ctypes.c_float, vp, vp], st),
         "fg_linear_bf16": ([vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp], st),
+        "fg_linear_qkv_bf16": ([vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                ctypes.c_int32, vp], st),
         "fg_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "fg_last_error": ([], ctypes.c_char_p),
     }
@@ -345,3 +348,10 @@ def fg_ragged_attention_noalloc(handle, dev: FgRaggedBatch, info: FgPlanInfo, wo
 def fg_linear_bf16(x_ptr, w_ptr, y_ptr, T, K, N, stream):
     """y[T][N] = x[T][K] . w[N][K]^T in bf16 (device pointers)."""
     _check(lib().fg_linear_bf16(x_ptr, w_ptr, y_ptr, int(T), int(K), int(N), stream))
+
+
+def fg_linear_qkv_bf16(x_ptr, wqkv_ptr, q_ptr, k_ptr, v_ptr, T, K, Nq, Nkv, stream):
+    """q[T][Nq], k[T][Nkv], v[T][Nkv] = x[T][K] . w_qkv[Nq + 2*Nkv][K]^T in bf16 (device
+    pointers; w_qkv stacks Wq, Wk and Wv)."""
+    _check(lib().fg_linear_qkv_bf16(x_ptr, wqkv_ptr, q_ptr, k_ptr, v_ptr, int(T), int(K),
+                                    int(Nq), int(Nkv), stream))

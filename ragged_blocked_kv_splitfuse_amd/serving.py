@@ -188,13 +188,15 @@ def latency_summary(ttft, pace, ttft_grid=(0.5, 1.0, 2.0), pace_grid=(0.025, 0.0
 
 
 class Projections:
-    """The dense projections of one attention layer (``fg_linear_bf16``): Q, K and V from the
-    pass's hidden rows x [T][hidden] (separate weights, so each lands in the dense layout the
-    pass reads), and the output projection of attention's rows."""
+    """The dense projections of one attention layer: Q, K and V from the pass's hidden rows
+    x [T][hidden] in one fused product over the stacked weights (``fg_linear_qkv_bf16``, each
+    result landing in the dense layout the pass reads), and the output projection of
+    attention's rows (``fg_linear_bf16``)."""
 
     def __init__(self, wq, wk, wv, wo, budget: int, stream=None):
         import torch
         self.wq, self.wk, self.wv, self.wo = wq, wk, wv, wo
+        self.w_qkv = torch.cat((wq, wk, wv), dim=0).contiguous()
         self.hidden = int(wq.shape[1])
         self.stream = stream
         dev, dt = wq.device, wq.dtype
@@ -208,8 +210,11 @@ class Projections:
                           int(w.shape[0]), stream_handle(self.stream))
 
     def qkv(self, x, T):
-        for w, y in ((self.wq, self.q), (self.wk, self.k), (self.wv, self.v)):
-            self._lin(x, w, y, T)
+        from .runtime import stream_handle
+        fg.fg_linear_qkv_bf16(x.data_ptr(), self.w_qkv.data_ptr(), self.q.data_ptr(),
+                              self.k.data_ptr(), self.v.data_ptr(), T, self.hidden,
+                              int(self.wq.shape[0]), int(self.wk.shape[0]),
+                              stream_handle(self.stream))
         return self.q[:T], self.k[:T], self.v[:T]
 
     def output(self, o, T):

@@ -602,3 +602,25 @@ def test_noalloc_rejects_plans_beyond_its_scratch():
                    None) == fg.FG_E_WORKSPACE
     assert "scratch" in fg.fg_last_error()
     fg.fg_blocked_cache_destroy(h)
+
+
+def test_linear_argument_errors():
+    """Both projection entry points reject bad arguments before launching anything (so this
+    runs without a GPU): T = 0 is a no-op, null or unaligned pointers and negative sizes are
+    FG_E_ARG, widths off the tile grid are FG_E_UNSUPPORTED."""
+    L = fg.lib()
+    a = 4096  # an aligned stand-in address: never dereferenced on these paths
+    qkv = L.fg_linear_qkv_bf16
+    assert qkv(None, None, None, None, None, 0, 64, 128, 128, None) == fg.FG_OK
+    assert qkv(None, None, None, None, None, 4, 64, 128, 128, None) == fg.FG_E_ARG
+    assert qkv(a, a, a, a, a + 8, 4, 64, 128, 128, None) == fg.FG_E_ARG
+    assert qkv(a, a, a, a, a, -1, 64, 128, 128, None) == fg.FG_E_ARG
+    assert qkv(a, a, a, a, a, 4, 64, 0, 128, None) == fg.FG_E_ARG
+    assert qkv(a, a, a, a, a, 4, 64, 128, 100, None) == fg.FG_E_UNSUPPORTED
+    assert qkv(a, a, a, a, a, 4, 96, 128, 128, None) == fg.FG_E_UNSUPPORTED
+    lin = L.fg_linear_bf16
+    assert lin(None, None, None, 0, 64, 128, None) == fg.FG_OK
+    assert lin(None, a, a, 4, 64, 128, None) == fg.FG_E_ARG
+    assert lin(a, a, a + 4, 4, 64, 128, None) == fg.FG_E_ARG
+    assert lin(a, a, a, 4, 64, 192, None) == fg.FG_E_UNSUPPORTED
+    assert lin(a, a, a, 4, 100, 128, None) == fg.FG_E_UNSUPPORTED
