@@ -398,17 +398,16 @@ void launch_skinny(const u16 *x, const u16 *w, const OutSeg &y, int T, int K, in
 // width is a multiple of 256 (the 256 x 256 tile may be used).
 fg_status run_linear(const u16 *xp, const u16 *wp, const OutSeg &o, int T, int K, int N,
                      bool wide_ok, hipStream_t st) {
-  // 256 x 256 tiles (eight waves, 64-wide stages, one workgroup per compute unit, the chip has
-  // 256) when there are at least ~140 of them in every round, the last included, and their
-  // token rows are at least 90% used; else 128 x 128 tiles (four waves, two workgroups per CU)
-  // when they put at least one workgroup on every CU; else 128 x 64 tiles.
-  // Measured on the projection shapes (K 4096; N 12288, 6144 and 4096; T 512 to 4100): the
-  // eight-wave 256 x 256 tiles run 3-13% faster than 128 x 128 from 144 workgroups on when
-  // every round is full, but lose 5-15% where the last round is partly empty and ~40% at
-  // T = 640 (a last token tile half empty); the four-wave 256 x 256 form they replace (one
-  // wave per SIMD) was 7-16% slower than them, and 256 x 128 tiles are now slower than
-  // 128 x 128 everywhere.  128 x 64 tiles win at up to 256 128 x 128 workgroups (one round
-  // of two per CU) and lose ~20% just above (a second round).
+  // Between the eight-wave 256 x 256 tile (one workgroup per compute unit, the chip has 256)
+  // and the four-wave 128 x 128 tile (two per CU), by rounds of workgroups: a full round takes
+  // ~111 us of the former and ~64 us of the latter at K = 4096 (both scale with K), so the
+  // 256 x 256 tile is taken when its rounds cost no more (partly empty rounds and half-empty
+  // token tiles count as full ones).  Measured on ~40 projection shapes (K 4096; N 1024 to
+  // 12288; T 512 to 4100) this picks the faster of the two everywhere but at ties (within 4%);
+  // e.g. T = 1040, N = 12288: 114 against 124 us (one round against two), T = 640: 67 us on
+  // 128 x 128 against 93 (one round each).  Below that, 128 x 64 tiles when 128 x 128 would
+  // not put a workgroup on every CU.  (The four-wave 256 x 256 form, one wave per SIMD, was
+  // 7-16% slower than the eight-wave one; 256 x 128 tiles are now slower than 128 x 128.)
   // Up to 64 token rows: the weight-streaming kernel (whole stages of 512 or 256 inner
   // elements).
   if (T <= 64 && K % 512 == 0) {
@@ -418,12 +417,12 @@ fg_status run_linear(const u16 *xp, const u16 *wp, const OutSeg &o, int T, int K
     else launch_skinny<4>(xp, wp, o, T, K, N, st);
   } else {
     const auto tiles = [&](int bm, int bn) { return (int64_t)((T + bm - 1) / bm) * (N / bn); };
-    constexpr int64_t CUS = 256, FULL = 140;
-    const int64_t t256 = wide_ok ? tiles(256, 256) : 0, rem = t256 % CUS;
-    const bool rows_used = 10 * (int64_t)T >= 9 * (int64_t)((T + 255) / 256 * 256);
-    if (t256 >= FULL && (rem == 0 || rem >= FULL) && rows_used)
+    constexpr int64_t CUS = 256, ROUND_256_US = 111, ROUND_128_US = 64;
+    const int64_t t256 = wide_ok ? tiles(256, 256) : 0, t128 = tiles(128, 128);
+    const int64_t rounds_256 = (t256 + CUS - 1) / CUS, rounds_128 = (t128 + 2 * CUS - 1) / (2 * CUS);
+    if (t256 > 0 && ROUND_256_US * rounds_256 <= ROUND_128_US * rounds_128)
       launch<2, 4, 64, 4, 2>(xp, wp, o, T, K, N, st);
-    else if (tiles(128, 128) > CUS)
+    else if (t128 > CUS)
       launch<2, 2, 64, 2, 2>(xp, wp, o, T, K, N, st);
     else
       launch<2, 1, 64, 2, 2>(xp, wp, o, T, K, N, st);

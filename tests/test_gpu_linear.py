@@ -22,9 +22,9 @@ SHAPES = [  # (T, K, N): LLaMA-2-7B q/k/v/o (4096 -> 4096), Mistral-7B k/v (4096
     # fused QKV width (12288); the token counts reach each kernel the GEMM picks (the
     # weight-streaming kernel with 1 to 4 16-token tiles up to 64 rows; above, 128 x 64 tiles
     # (T = 512, 3000 at N = 1024), 128 x 128 (T = 2048, 4100 at N = 4096; T = 640 at
-    # N = 12288, whose last 256-token tile would be too empty) and the eight-wave 256 x 256 tile
-    # (T = 1174 and 700 at N = 12288, T = 3000 at N = 4096)), with ragged tails, and N = 1536
-    # the tile placement without the per-XCD split
+    # N = 12288, where 128 x 128 needs one round as 256 x 256 does) and the eight-wave
+    # 256 x 256 tile (T = 1174 and 700 at N = 12288, T = 3000 at N = 4096)), with ragged
+    # tails, and N = 1536 the tile placement without the per-XCD split
     (1, 4096, 4096), (17, 4096, 4096), (22, 4096, 1024), (37, 4096, 4096), (64, 4096, 1024),
     (512, 4096, 1024), (2048, 4096, 4096), (3000, 4096, 1024), (4100, 4096, 4096),
     (1174, 4096, 12288), (700, 4096, 12288), (640, 4096, 12288), (3000, 4096, 4096),
@@ -69,7 +69,7 @@ def test_linear_repeated_calls_and_shapes_share_state():
 QKV_SHAPES = [  # (T, K, Nq, Nkv): LLaMA-2-7B (4096 / 4096) and Mistral-7B (4096 / 1024) widths at
     # token counts that reach the weight-streaming kernel (T <= 64), the eight-wave 256 x 256
     # tile (T = 700 and 1174 at N = 12288, 2048 at N = 6144) and the 128 x 128 tile (T = 2048
-    # at N = 12288, a partly empty last round; T = 1174 at N = 6144); and widths that are
+    # at N = 12288, fewer rounds; T = 1174 at N = 6144); and widths that are
     # multiples of 128 but not 256 (the column boundaries then fall inside a 256-wide span)
     (17, 4096, 4096, 4096), (700, 4096, 4096, 4096), (1174, 4096, 4096, 4096),
     (2048, 4096, 4096, 4096), (40, 4096, 4096, 1024), (1174, 4096, 4096, 1024),
