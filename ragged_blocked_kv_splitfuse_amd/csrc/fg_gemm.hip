@@ -12,14 +12,15 @@
 // that every SIMD has two waves to issue its matrix instructions from.  The MFMA computes the
 // transposed product C^T = W . X^T (A operand: 32 weight rows, B operand: 32 token rows; both
 // rows are contiguous along K, so every operand is one 16-byte load), which leaves each lane
-// with runs of four consecutive output features of one token: 8-byte stores of y rows.  The
+// with runs of four consecutive output features of one token: 8-byte stores into the output
+// matrix those columns belong to (y, or q, k and v for the fused QKV projection).  The
 // inner dimension advances in BK-element stages; each stage's weight and token rows go from
 // memory straight into LDS with 16-byte LDS-DMA loads through an NSTG-deep ring, each buffer
 // refilled as soon as every wave has read it, swizzled so that the operand reads are free of
 // bank conflicts.  The operand reads run one MFMA k-step ahead of the products (two register
 // sets), interleaved with them, so the matrix cores do not wait for LDS.  The host
-// picks the tile by the number of workgroups it gives (ragged token counts run from a few rows
-// to thousands).  Tiles are placed per XCD where the shape allows (workgroup
+// picks the tile by the rounds of workgroups each would need (ragged token counts run from a
+// few rows to thousands).  Tiles are placed per XCD where the shape allows (workgroup
 // b runs on XCD b % 8): each XCD takes a contiguous eighth of the output features, so its L2
 // holds that eighth of the weights while the token rows stream.
 #include <hip/hip_runtime.h>
